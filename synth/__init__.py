@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for the chunked flash-attention forward.
+
+This module is shared by the fp64 oracle's tests, the GPU parity tests and the
+benchmark.  It holds no attention arithmetic: it only draws random tensors,
+builds sequence-length prefix sums, page tables and per-tensor fp8 codes.
+
+Workload shapes (the five workloads of the method's pages, restated):
+  * tiny causal GQA:      B=1, Hq=2,  Hkv=1, N=300,  D=64,  bf16
+  * dense prefill:        B=1, Hq=Hkv=32,   N=8192, D=128, bf16
+  * causal GQA varlen:    B=4, Hq=32, Hkv=8, lengths {4096, 2500, 1, 3969}, D=128
+  * split-KV paged decode: 64 sequences x 1 token, Hq=32, Hkv=8, D=128,
+                          context lengths uniform in [1, 32768], page size 16
+  * fp8 wide-head prefill: B=1, Hq=Hkv=32, N=8192, D=192, e4m3 per-tensor scaled
+
+All values are N(0,1) and unscaled (scaled fixtures hide corruption: ffpa-attn
+PR "fp8 attention D=192" page, section "Tests / docs").  Tensors are produced on
+the CPU with ``torch.Generator`` so that the same seed gives the same bytes on
+every machine.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0  # largest finite OCP E4M3FN value
+
+TINY_CAUSAL = dict(name="tiny_causal_gqa", seqlens=[300], hq=2, hkv=1, d=64, causal=True)
+DENSE_PREFILL = dict(name="dense_prefill", seqlens=[8192], hq=32, hkv=32, d=128, causal=False)
+CAUSAL_VARLEN = dict(name="causal_gqa_varlen", seqlens=[4096, 2500, 1, 3969], hq=32, hkv=8, d=128,
+                     causal=True)
+PAGED_DECODE = dict(name="paged_decode", batch=64, hq=32, hkv=8, d=128, page_size=16,
+                    ctx_min=1, ctx_max=32768, spare_pages=1024)
+FP8_WIDE = dict(name="fp8_wide_head", seqlens=[8192], hq=32, hkv=32, d=192)
+
+
+def _gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def cu_seqlens(lengths: Sequence[int]) -> torch.Tensor:
+    """Exclusive prefix sum [0, l0, l0+l1, ...] as int32 (CPU)."""
+    out = np.zeros(len(lengths) + 1, dtype=np.int64)
+    out[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    assert out[-1] < 2**31
+    return torch.from_numpy(out.astype(np.int32))
+
+
+def randn_bf16(shape, gen: torch.Generator) -> torch.Tensor:
+    """N(0,1) drawn in fp32 then rounded to bf16 (round-to-nearest-even)."""
+    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+@dataclasses.dataclass
+class Fp8Tensor:
+    """Per-tensor scaled OCP E4M3FN codes: value = decode(codes) * scale."""
+    codes: torch.Tensor  # uint8, same shape as the source tensor
+    scale: float         # fp32 dequantisation scale (amax / 448)
+
+
+def quantize_e4m3(x: torch.Tensor) -> Fp8Tensor:
+    """Per-tensor amax/448 scale, round-to-nearest-even into E4M3FN, saturating."""
+    x = x.float()
+    amax = float(x.abs().max())
+    scale = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+    y = (x / float(scale)).clamp(-E4M3_MAX, E4M3_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return Fp8Tensor(codes=codes.contiguous(), scale=float(scale))
+
+
+@dataclasses.dataclass
+class PrefillInputs:
+    q: torch.Tensor            # [total_q, Hq, D]  bf16 (or uint8 codes for fp8)
+    k: torch.Tensor            # [total_k, Hkv, D]
+    v: torch.Tensor            # [total_k, Hkv, D]
+    cu_seqlens_q: torch.Tensor  # int32 [B+1]
+    cu_seqlens_k: torch.Tensor  # int32 [B+1]
+    seqlens_q: list
+    seqlens_k: list
+    hq: int
+    hkv: int
+    d: int
+    scale: float
+    causal: bool
+    dtype: str = "bf16"
+    q_scale: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    seed: int = 0
+
+
+def prefill_inputs(seed: int, seqlens_q: Sequence[int], hq: int, hkv: int, d: int,
+                   causal: bool, seqlens_k: Optional[Sequence[int]] = None,
+                   dtype: str = "bf16", scale: Optional[float] = None) -> PrefillInputs:
+    """Packed-varlen Q/K/V ~ N(0,1) for one prefill (or extend, when q_len < k_len) call."""
+    seqlens_q = [int(x) for x in seqlens_q]
+    seqlens_k = [int(x) for x in (seqlens_k if seqlens_k is not None else seqlens_q)]
+    assert len(seqlens_q) == len(seqlens_k)
+    tq, tk = sum(seqlens_q), sum(seqlens_k)
+    g = _gen(seed)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    if dtype == "bf16":
+        q = randn_bf16((tq, hq, d), g)
+        k = randn_bf16((tk, hkv, d), g)
+        v = randn_bf16((tk, hkv, d), g)
+        return PrefillInputs(q, k, v, cu_seqlens(seqlens_q), cu_seqlens(seqlens_k), seqlens_q,
+                             seqlens_k, hq, hkv, d, float(scale), bool(causal), "bf16", seed=seed)
+    if dtype == "fp8":
+        qf = quantize_e4m3(torch.randn(tq, hq, d, generator=g))
+        kf = quantize_e4m3(torch.randn(tk, hkv, d, generator=g))
+        vf = quantize_e4m3(torch.randn(tk, hkv, d, generator=g))
+        return PrefillInputs(qf.codes, kf.codes, vf.codes, cu_seqlens(seqlens_q),
+                             cu_seqlens(seqlens_k), seqlens_q, seqlens_k, hq, hkv, d, float(scale),
+                             bool(causal), "fp8", qf.scale, kf.scale, vf.scale, seed=seed)
+    raise ValueError(dtype)
+
+
+@dataclasses.dataclass
+class DecodeInputs:
+    q: torch.Tensor            # [B, Hq, D] bf16
+    k_cache: torch.Tensor      # [num_pages, page_size, Hkv, D] bf16
+    v_cache: torch.Tensor      # [num_pages, page_size, Hkv, D] bf16
+    page_table: torch.Tensor   # int32 [B, max_pages_per_seq]
+    context_lens: torch.Tensor  # int32 [B]
+    hq: int
+    hkv: int
+    d: int
+    page_size: int
+    scale: float
+    seed: int = 0
+    dtype: str = "bf16"
+    q_scale: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+
+def decode_inputs(seed: int, batch: int, hq: int, hkv: int, d: int, page_size: int = 16,
+                  context_lens: Optional[Sequence[int]] = None, ctx_min: int = 1,
+                  ctx_max: int = 32768, spare_pages: int = 1024, poison: bool = True,
+                  scale: Optional[float] = None, dtype: str = "bf16") -> DecodeInputs:
+    """Paged KV cache with a seeded random page table.
+
+    Live slots are N(0,1); slots past a sequence's context length and spare pages
+    hold NaN when ``poison`` is set, so any read of a dead slot shows in the output.
+    The table has ``ceil(max_ctx / page_size)`` columns; unused entries point at
+    spare pages (or page 0 when there are none).
+    """
+    g = _gen(seed)
+    if context_lens is None:
+        ctx = torch.randint(ctx_min, ctx_max + 1, (batch,), generator=g, dtype=torch.int64)
+    else:
+        ctx = torch.tensor([int(c) for c in context_lens], dtype=torch.int64)
+        assert len(ctx) == batch
+    pages = [(int(c) + page_size - 1) // page_size for c in ctx]
+    num_pages = sum(pages) + spare_pages
+    max_pages = max(1, max(pages) if pages else 1)
+    perm = torch.randperm(num_pages, generator=g)
+    table = torch.empty(batch, max_pages, dtype=torch.int32)
+    pos = 0
+    filler = perm[sum(pages):] if spare_pages > 0 else torch.zeros(1, dtype=torch.int64)
+    for b in range(batch):
+        n = pages[b]
+        table[b, :n] = perm[pos:pos + n].to(torch.int32)
+        pos += n
+        rest = max_pages - n
+        if rest > 0:
+            table[b, n:] = filler[torch.arange(rest) % len(filler)].to(torch.int32)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    q32 = torch.randn(batch, hq, d, generator=g)
+    k32 = torch.randn(num_pages, page_size, hkv, d, generator=g)
+    v32 = torch.randn(num_pages, page_size, hkv, d, generator=g)
+    if poison:
+        live = torch.zeros(num_pages, page_size, dtype=torch.bool)
+        for b in range(batch):
+            c = int(ctx[b])
+            for j in range(pages[b]):
+                p = int(table[b, j])
+                live[p, : min(page_size, c - j * page_size)] = True
+        k32[~live] = float("nan")
+        v32[~live] = float("nan")
+    if dtype == "bf16":
+        return DecodeInputs(q32.to(torch.bfloat16), k32.to(torch.bfloat16), v32.to(torch.bfloat16),
+                            table, ctx.to(torch.int32), hq, hkv, d, page_size, float(scale), seed)
+    if dtype == "fp8":
+        qf = quantize_e4m3(q32)
+        kf = quantize_e4m3(torch.nan_to_num(k32, nan=0.0))
+        vf = quantize_e4m3(torch.nan_to_num(v32, nan=0.0))
+        kc, vc = kf.codes.clone(), vf.codes.clone()
+        if poison:
+            kc[~live] = 0x7F  # E4M3FN NaN code
+            vc[~live] = 0x7F
+        return DecodeInputs(qf.codes, kc, vc, table, ctx.to(torch.int32), hq, hkv, d, page_size,
+                            float(scale), seed, "fp8", qf.scale, kf.scale, vf.scale)
+    raise ValueError(dtype)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a bf16/fp32 CPU tensor to a float64 NumPy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def workload_prefill(cfg: dict, seed: int, dtype: str = "bf16", causal: Optional[bool] = None):
+    c = cfg["causal"] if causal is None else causal
+    return prefill_inputs(seed, cfg["seqlens"], cfg["hq"], cfg["hkv"], cfg["d"], c, dtype=dtype)

@@ -1,0 +1,324 @@
+"""Pins for the fp64 oracle, checked against things other than itself.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped scale, a
+wrong causal offset, a transposed operand, a merge without rescale, a wrong
+GQA map, a wrong E4M3 field) fails at least one of them; ``test_planted_*``
+plant such slips into the oracle on the CPU and check that a pin catches each.
+
+The definition being pinned is the attention forward served by the chunked
+kernel on the RL-Kernel "MFMA batch-invariant GEMM and chunked Triton
+attention" page, section 2.  No page prints a worked attention example, so the
+pins are brute force, closed forms and invariants.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.fp64 as oatt
+
+RNG = np.random.default_rng(1234)
+
+
+def brute_force(q, k, v, cu_q, cu_k, hq, hkv, scale, causal):
+    """Textbook softmax attention with explicit Python loops and math.exp."""
+    tq, _, d = q.shape
+    out = [[[0.0] * d for _ in range(hq)] for _ in range(tq)]
+    lse = [[-math.inf] * hq for _ in range(tq)]
+    grp = hq // hkv
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        lq, lk = q1 - q0, k1 - k0
+        for h in range(hq):
+            g = h // grp
+            for i in range(lq):
+                keys = [j for j in range(lk) if (not causal) or j <= i + lk - lq]
+                if not keys:
+                    continue
+                s = []
+                for j in keys:
+                    dot = 0.0
+                    for t in range(d):
+                        dot += float(q[q0 + i, h, t]) * float(k[k0 + j, g, t])
+                    s.append(scale * dot)
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                z = sum(w)
+                for t in range(d):
+                    out[q0 + i][h][t] = sum(w[n] * float(v[k0 + j, g, t]) for n, j in enumerate(keys)) / z
+                lse[q0 + i][h] = mx + math.log(z)
+    return np.array(out, dtype=np.float64).reshape(tq, hq, d), np.array(lse).reshape(tq, hq)
+
+
+def make(seqlens_q, seqlens_k, hq, hkv, d, seed=0, scale_v=1.0):
+    rng = np.random.default_rng(seed)
+    tq, tk = sum(seqlens_q), sum(seqlens_k)
+    q = rng.standard_normal((tq, hq, d))
+    k = rng.standard_normal((tk, hkv, d))
+    v = rng.standard_normal((tk, hkv, d)) * scale_v
+    cu_q = np.concatenate([[0], np.cumsum(seqlens_q)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(seqlens_k)]).astype(np.int64)
+    return q, k, v, cu_q, cu_k
+
+
+SMALL_CASES = [
+    # (seqlens_q, seqlens_k, hq, hkv, d, causal)
+    ([7], [7], 2, 1, 5, True),
+    ([7], [7], 2, 2, 4, False),
+    ([3, 9, 1], [3, 9, 1], 4, 2, 3, True),
+    ([2, 5], [6, 11], 2, 1, 4, True),      # extend: q_len < k_len, bottom-right aligned
+    ([6, 3], [4, 3], 2, 1, 3, True),       # q_len > k_len: leading rows see no key
+    ([4, 0, 5], [4, 0, 5], 3, 1, 2, False),  # an empty sequence in the batch
+    ([5], [0], 1, 1, 3, False),            # zero keys
+]
+
+
+@pytest.mark.parametrize("case", SMALL_CASES)
+def test_plain_matches_brute_force(case):
+    sq, sk, hq, hkv, d, causal = case
+    q, k, v, cu_q, cu_k = make(sq, sk, hq, hkv, d, seed=len(sq) * 7 + d)
+    scale = 0.37
+    o, l = oracle.attention(q, k, v, cu_q, cu_k, hq, hkv, scale, causal)
+    ob, lb = brute_force(q, k, v, cu_q, cu_k, hq, hkv, scale, causal)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(l), np.isneginf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(l[fin], lb[fin], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lens", [([1300], [1300]), ([70, 700], [600, 1100]), ([513, 64], [513, 64])])
+def test_chunked_equals_plain(causal, lens):
+    """The chunked evaluation (64-key blocks in 512-key chunks, ascending exact
+    rescale) equals the plain definition up to fp64 rounding: the rescale is an
+    algebraic identity, so this pins the algorithm's steps."""
+    sq, sk = lens
+    q, k, v, cu_q, cu_k = make(sq, sk, 4, 2, 8, seed=sum(sq))
+    o1, l1 = oracle.attention(q, k, v, cu_q, cu_k, 4, 2, 1 / math.sqrt(8), causal)
+    o2, l2 = oracle.attention_chunked(q, k, v, cu_q, cu_k, 4, 2, 1 / math.sqrt(8), causal)
+    np.testing.assert_allclose(o2, o1, rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(l1), np.isneginf(l2))
+    fin = np.isfinite(l1)
+    np.testing.assert_allclose(l2[fin], l1[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_chunk_partials_start_empty_and_cover_absolute_keys():
+    """Chunk c's partial only sees keys [512c, 512c+512): with V one-hot on the
+    chunk index, acc_c / l_c is exactly the indicator of chunk c."""
+    lk, d = 1500, 4
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, d))
+    k = rng.standard_normal((lk, d))
+    v = np.zeros((lk, 3))
+    v[np.arange(lk), np.arange(lk) // 512] = 1.0
+    parts = oatt.chunk_partials(q, k, v, np.array([0]), 1, lk, 0.5, False)
+    assert len(parts) == 3
+    for c, (m, l, acc) in enumerate(parts):
+        expect = np.zeros(3)
+        expect[c] = 1.0
+        np.testing.assert_allclose(acc[0] / l[0], expect, atol=1e-15)
+        # m_c is the max of the chunk's own scores
+        assert m[0] == pytest.approx(np.max(0.5 * (k[512 * c:512 * (c + 1)] @ q[0])), rel=1e-15)
+
+
+def test_rows_sum_to_one():
+    q, k, v, cu_q, cu_k = make([300, 45], [300, 45], 2, 1, 6, seed=5)
+    for causal in (False, True):
+        o, _ = oracle.attention(q, k, np.ones_like(v), cu_q, cu_k, 2, 1, 0.8, causal)
+        np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-13)
+        o, _ = oracle.attention_chunked(q, k, np.ones_like(v), cu_q, cu_k, 2, 1, 0.8, causal)
+        np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-13)
+
+
+def test_key_permutation_invariance_dense():
+    q, k, v, cu_q, cu_k = make([40], [700], 2, 2, 5, seed=9)
+    perm = RNG.permutation(700)
+    o1, l1 = oracle.attention(q, k, v, cu_q, cu_k, 2, 2, 0.5, False)
+    o2, l2 = oracle.attention(q, k[perm], v[perm], cu_q, cu_k, 2, 2, 0.5, False)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l2, l1, rtol=1e-13)
+
+
+def test_all_masked_rows():
+    # q_len > k_len under bottom-right alignment: the first q_len - k_len rows see no key.
+    q, k, v, cu_q, cu_k = make([10], [4], 2, 1, 3, seed=2)
+    for fn in (oracle.attention, oracle.attention_chunked):
+        o, l = fn(q, k, v, cu_q, cu_k, 2, 1, 1.0, True)
+        assert np.all(o[:6] == 0.0) and np.all(np.isneginf(l[:6]))
+        assert np.all(np.isfinite(l[6:]))
+    # zero keys
+    q, k, v, cu_q, cu_k = make([3], [0], 1, 1, 2, seed=2)
+    o, l = oracle.attention(q, k, v, cu_q, cu_k, 1, 1, 1.0, False)
+    assert np.all(o == 0.0) and np.all(np.isneginf(l))
+
+
+def test_closed_forms():
+    q, k, v, cu_q, cu_k = make([17, 1, 33], [17, 1, 33], 2, 1, 4, seed=11)
+    o, l = oracle.attention(q, k, v, cu_q, cu_k, 2, 1, 0.7, True)
+    # causal row 0 sees only key 0: O = V[0] and lse = scale * q0.k0
+    for b in range(3):
+        r = cu_q[b]
+        for h in range(2):
+            np.testing.assert_array_equal(o[r, h], v[cu_k[b], 0])
+            assert l[r, h] == pytest.approx(0.7 * q[r, h] @ k[cu_k[b], 0], rel=1e-14)
+    # q = 0: every visible key has score 0, so O is the mean of the visible V rows
+    q0 = np.zeros_like(q)
+    o, l = oracle.attention(q0, k, v, cu_q, cu_k, 2, 1, 0.7, True)
+    for i in range(33):
+        np.testing.assert_allclose(o[cu_q[2] + i, 1], v[cu_k[2]:cu_k[2] + i + 1, 0].mean(axis=0),
+                                   rtol=1e-13, atol=1e-14)
+        assert l[cu_q[2] + i, 1] == pytest.approx(math.log(i + 1), abs=1e-13)
+    # one dominant score: O is that key's value row
+    k2 = k.copy()
+    q2 = np.zeros_like(q)
+    q2[:, :, 0] = 1.0
+    k2[:, :, 0] = 0.0
+    k2[cu_k[2] + 5, 0, 0] = 2000.0
+    o, _ = oracle.attention(q2, k2, v, cu_q, cu_k, 2, 1, 1.0, False)
+    np.testing.assert_allclose(o[cu_q[2]:cu_q[3], 0], np.broadcast_to(v[cu_k[2] + 5, 0], (33, 4)),
+                               atol=1e-300)
+
+
+def test_two_key_closed_form():
+    """softmax over two keys: weights e^a/(e^a+e^b), e^b/(e^a+e^b)."""
+    q = np.array([[[1.0, 2.0]]])
+    k = np.array([[[1.0, 0.0]], [[0.0, 1.0]]])
+    v = np.array([[[10.0, -1.0]], [[4.0, 3.0]]])
+    o, l = oracle.attention(q, k, v, [0, 1], [0, 2], 1, 1, 0.5, False)
+    a, b = 0.5, 1.0
+    wa, wb = math.exp(a) / (math.exp(a) + math.exp(b)), math.exp(b) / (math.exp(a) + math.exp(b))
+    np.testing.assert_allclose(o[0, 0], [10 * wa + 4 * wb, -1 * wa + 3 * wb], rtol=1e-15)
+    assert l[0, 0] == pytest.approx(math.log(math.exp(a) + math.exp(b)), rel=1e-15)
+
+
+def test_gqa_equals_repeated_mha():
+    q, k, v, cu_q, cu_k = make([50, 20], [50, 20], 6, 2, 4, seed=4)
+    o1, _ = oracle.attention(q, k, v, cu_q, cu_k, 6, 2, 0.3, True)
+    o2, _ = oracle.attention(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), cu_q, cu_k, 6, 6,
+                             0.3, True)
+    np.testing.assert_array_equal(o1, o2)
+
+
+def test_rows_subset_matches_full():
+    q, k, v, cu_q, cu_k = make([100, 37], [100, 37], 2, 1, 4, seed=6)
+    o, l = oracle.attention(q, k, v, cu_q, cu_k, 2, 1, 0.4, True)
+    rows = [0, 5, 99, 100, 136]
+    os_, ls = oracle.attention(q, k, v, cu_q, cu_k, 2, 1, 0.4, True, rows=rows)
+    np.testing.assert_array_equal(os_[rows], o[rows])
+    np.testing.assert_array_equal(ls[rows], l[rows])
+    assert np.isnan(os_[1]).all()
+
+
+def test_e4m3fn_table_spec_values():
+    t = oracle.e4m3fn_table()
+    assert t[0x00] == 0.0 and t[0x80] == 0.0 and math.copysign(1, t[0x80]) == -1
+    assert t[0x38] == 1.0            # exponent 7 = bias
+    assert t[0x7E] == 448.0          # largest finite
+    assert t[0xFE] == -448.0
+    assert t[0x08] == 2.0 ** -6      # smallest normal
+    assert t[0x01] == 2.0 ** -9      # smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9  # largest subnormal
+    assert math.isnan(t[0x7F]) and math.isnan(t[0xFF])
+    fin = t[np.isfinite(t)]
+    assert len(fin) == 254 and not np.isinf(t).any()
+    pos = t[1:0x7F]
+    assert np.all(np.diff(pos) > 0)  # codes 0x01..0x7E increase monotonically
+
+
+def test_paged_decode_is_last_prefill_row():
+    """A decode token at position ctx-1 equals the last row of the causal prefill
+    of the same sequence (bottom-right alignment), whatever the page order."""
+    rng = np.random.default_rng(8)
+    hq, hkv, d, ps = 4, 2, 5, 16
+    ctxs = [1, 16, 17, 100]
+    seqs = [(rng.standard_normal((c, hq, d)), rng.standard_normal((c, hkv, d)),
+             rng.standard_normal((c, hkv, d))) for c in ctxs]
+    npages = sum((c + ps - 1) // ps for c in ctxs) + 3
+    perm = rng.permutation(npages)
+    kc = np.full((npages, ps, hkv, d), np.nan)
+    vc = np.full((npages, ps, hkv, d), np.nan)
+    table = np.zeros((len(ctxs), 7), dtype=np.int64)
+    pos = 0
+    for b, c in enumerate(ctxs):
+        for j in range(c):
+            if j % ps == 0:
+                table[b, j // ps] = perm[pos]
+                pos += 1
+            kc[table[b, j // ps], j % ps] = seqs[b][1][j]
+            vc[table[b, j // ps], j % ps] = seqs[b][2][j]
+    qd = np.stack([s[0][-1] for s in seqs])
+    o, l = oracle.paged_decode(qd, kc, vc, table, ctxs, hq, hkv, 0.45, ps)
+    for b, c in enumerate(ctxs):
+        qs, ks, vs = seqs[b]
+        op, lp = brute_force(qs, ks, vs, [0, c], [0, c], hq, hkv, 0.45, True)
+        np.testing.assert_allclose(o[b], op[-1], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(l[b], lp[-1], rtol=1e-12)
+
+
+def test_flop_counts():
+    f = oracle.attention_flops
+    # dense: 4 * N^2 * D * H
+    assert f([8192], [8192], 32, 128, False) == 4 * 8192 * 8192 * 128 * 32
+    # causal, q_len == k_len: N(N+1)/2 pairs per head
+    assert f([300], [300], 2, 64, True) == 4 * 64 * 2 * (300 * 301 // 2)
+    lens = [4096, 2500, 1, 3969]
+    assert f(lens, lens, 32, 128, True) == 4 * 128 * 32 * sum(n * (n + 1) // 2 for n in lens)
+    # extend: the last row sees all keys
+    assert f([2], [5], 1, 1, True) == 4 * (4 + 5)
+    # q_len > k_len: leading rows see nothing
+    assert f([5], [2], 1, 1, True) == 4 * (0 + 0 + 0 + 1 + 2)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: each slip below is injected into the oracle (on the CPU) and
+# at least one pin above must fail on it.
+# ---------------------------------------------------------------------------
+def _fails(fn):
+    try:
+        fn()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_top_left_causal_alignment(monkeypatch):
+    def top_left(rows, lq, lk, causal):
+        j = np.arange(lk)[None, :]
+        ok = (j <= np.asarray(rows)[:, None]) if causal else (j < lk)
+        return np.broadcast_to(ok, (len(rows), lk)).copy()
+    monkeypatch.setattr(oatt, "visible", top_left)
+    assert _fails(lambda: test_plain_matches_brute_force(SMALL_CASES[3]))
+
+
+def test_planted_merge_without_rescale(monkeypatch):
+    def bad_merge(total, part):
+        M, L, A = total
+        m, l, acc = part
+        live = m > -np.inf
+        return (np.where(live, np.maximum(M, m), M), L + np.where(live, l, 0),
+                A + np.where(live[:, None], acc, 0))
+    monkeypatch.setattr(oatt, "_merge", bad_merge)
+    assert _fails(lambda: test_chunked_equals_plain(False, ([1300], [1300])))
+
+
+def test_planted_block_update_without_alpha(monkeypatch):
+    orig = oatt._block_update
+
+    def no_alpha(state, s, vb):
+        m, l, acc = state
+        mblk = s.max(axis=1, initial=-np.inf)
+        live = mblk > -np.inf
+        m_new = np.where(live, np.maximum(m, mblk), m)
+        p = np.where(live[:, None], np.exp(s - np.where(live, m_new, 0.0)[:, None]), 0.0)
+        return m_new, l + p.sum(axis=1), acc + p @ vb
+    monkeypatch.setattr(oatt, "_block_update", no_alpha)
+    assert _fails(lambda: test_chunked_equals_plain(True, ([1300], [1300])))
+    monkeypatch.setattr(oatt, "_block_update", orig)
+
+
+def test_planted_e4m3_bias(monkeypatch):
+    t = oracle.e4m3fn_table()
+    bad = t * 2.0  # an exponent bias of 6 instead of 7
+    monkeypatch.setattr(oracle, "e4m3fn_table", lambda: bad)
+    assert _fails(test_e4m3fn_table_spec_values)
