@@ -1,0 +1,220 @@
+"""Python binding of libdetattn.so: argument marshalling only.
+
+The functions named like the C entry points (``attn_prefill_fwd``,
+``attn_decode_split_fwd``, ``attn_chunk_merge``, ``attn_partials_bytes``,
+``attn_num_chunks``, ``attn_status_str``) take torch tensors that already live
+on the GPU, pass their device pointers and sizes to the C ABI and raise
+``DetAttnError`` on a non-zero status.  ``prefill`` and ``decode`` additionally
+allocate the outputs (and the partials of the split schedule) with torch and
+chain the split and merge launches on the current stream.  Every step of the
+computation runs in the HIP kernels of the library; there is no fallback: if the
+library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "DetAttnError", "BF16", "FP8_E4M3", "MONOLITHIC", "SPLIT", "BLOCK_KEYS", "CHUNK_KEYS",
+    "PAGE_SIZE", "library_path", "load_library", "attn_status_str", "attn_num_chunks",
+    "attn_partials_bytes", "attn_prefill_fwd", "attn_decode_split_fwd", "attn_chunk_merge",
+    "prefill", "decode",
+]
+
+BF16, FP8_E4M3 = 0, 1
+MONOLITHIC, SPLIT = 0, 1
+BLOCK_KEYS, CHUNK_KEYS, PAGE_SIZE = 64, 512, 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+
+class DetAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {attn_status_str(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libdetattn.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the in-tree HIP library; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m deterministic_flash_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    c_i32, c_i64, c_f32, c_sz, c_p = (ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                                      ctypes.c_size_t, ctypes.c_void_p)
+    lib.attn_status_str.argtypes = [ctypes.c_int]
+    lib.attn_status_str.restype = ctypes.c_char_p
+    lib.attn_num_chunks.argtypes = [c_i32]
+    lib.attn_num_chunks.restype = c_i32
+    lib.attn_partials_bytes.argtypes = [c_i64, c_i32, c_i32, c_i32]
+    lib.attn_partials_bytes.restype = c_sz
+    lib.attn_prefill_fwd.argtypes = [c_i32, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i64,
+                                     c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_f32, c_f32, c_f32,
+                                     c_i32, c_p, c_p, c_p, c_sz, c_p]
+    lib.attn_prefill_fwd.restype = ctypes.c_int
+    lib.attn_decode_split_fwd.argtypes = [c_i32, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p,
+                                          c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                          c_f32, c_f32, c_f32, c_f32, c_i32, c_p, c_sz, c_p, c_p,
+                                          c_p]
+    lib.attn_decode_split_fwd.restype = ctypes.c_int
+    lib.attn_chunk_merge.argtypes = [c_p, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p]
+    lib.attn_chunk_merge.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the C ABI must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise DetAttnError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------- C-ABI mirrors
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def attn_num_chunks(max_seqlen_k: int) -> int:
+    return int(load_library().attn_num_chunks(int(max_seqlen_k)))
+
+
+def attn_partials_bytes(rows: int, num_heads_q: int, max_chunks: int, head_dim: int) -> int:
+    return int(load_library().attn_partials_bytes(int(rows), int(num_heads_q), int(max_chunks),
+                                                  int(head_dim)))
+
+
+def attn_prefill_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                     softmax_scale: float, causal: bool, schedule: int = MONOLITHIC,
+                     o=None, lse=None, partials=None, descales=(1.0, 1.0, 1.0),
+                     stream=None) -> None:
+    """Mirror of the C ``attn_prefill_fwd``; outputs are caller-provided tensors."""
+    lib = load_library()
+    st = lib.attn_prefill_fwd(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        int(cu_seqlens_q.numel() - 1), int(max_seqlen_q), int(max_seqlen_k), int(q.shape[0]),
+        int(k.shape[0]), int(q.shape[1]), int(k.shape[1]), int(q.shape[2]), float(softmax_scale),
+        int(bool(causal)), float(descales[0]), float(descales[1]), float(descales[2]),
+        int(schedule), _ptr(o), _ptr(lse), _ptr(partials),
+        0 if partials is None else partials.numel() * partials.element_size(), _stream(stream))
+    _check("attn_prefill_fwd", st)
+
+
+def attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
+                          softmax_scale: float, schedule: int = SPLIT, partials=None, o=None,
+                          lse=None, descales=(1.0, 1.0, 1.0), stream=None) -> None:
+    """Mirror of the C ``attn_decode_split_fwd`` for caches shaped
+    [num_pages, 16, Hkv, D] (contiguous)."""
+    lib = load_library()
+    npages, psize, hkv, d = k_cache.shape
+    st = lib.attn_decode_split_fwd(
+        _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(npages),
+        int(psize * hkv * d), int(hkv * d), int(d), _ptr(page_table), int(page_table.shape[1]),
+        _ptr(context_lens), int(max_context_len), int(q.shape[0]), int(psize), int(q.shape[1]),
+        int(hkv), int(d), float(softmax_scale), float(descales[0]), float(descales[1]),
+        float(descales[2]), int(schedule), _ptr(partials),
+        0 if partials is None else partials.numel() * partials.element_size(), _ptr(o),
+        _ptr(lse), _stream(stream))
+    _check("attn_decode_split_fwd", st)
+
+
+def attn_chunk_merge(partials, rows: int, num_heads_q: int, max_chunks: int, head_dim: int,
+                     o, lse=None, v_descale: float = 1.0, stream=None) -> None:
+    """Mirror of the C ``attn_chunk_merge``."""
+    lib = load_library()
+    st = lib.attn_chunk_merge(_ptr(partials),
+                              0 if partials is None else partials.numel() * partials.element_size(),
+                              int(rows), int(num_heads_q), int(max_chunks), int(head_dim),
+                              float(v_descale), _ptr(o), _ptr(lse), _stream(stream))
+    _check("attn_chunk_merge", st)
+
+
+# ------------------------------------------------------------- conveniences
+def _new_partials(rows: int, hq: int, cmax: int, d: int, device) -> torch.Tensor:
+    nbytes = attn_partials_bytes(rows, hq, cmax, d)
+    return torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=device)
+
+
+def prefill(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+            causal: bool, softmax_scale: Optional[float] = None, schedule: int = MONOLITHIC,
+            descales=(1.0, 1.0, 1.0), out: Optional[torch.Tensor] = None,
+            return_lse: bool = False, stream=None):
+    """Packed-varlen attention forward; returns O (bf16) and optionally lse.
+
+    With ``schedule=SPLIT`` the chunk partials go to a workspace and
+    ``attn_chunk_merge`` folds them on the same stream."""
+    tq, hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty(tq, hq, d, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(tq, hq, dtype=torch.float32, device=q.device) if return_lse else None
+    if schedule == SPLIT:
+        cmax = attn_num_chunks(max_seqlen_k)
+        part = _new_partials(tq, hq, cmax, d, q.device)
+        attn_prefill_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                         softmax_scale, causal, SPLIT, partials=part, descales=descales,
+                         stream=stream)
+        attn_chunk_merge(part, tq, hq, cmax, d, o, lse, v_descale=descales[2], stream=stream)
+    else:
+        attn_prefill_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                         softmax_scale, causal, MONOLITHIC, o=o, lse=lse, descales=descales,
+                         stream=stream)
+    return (o, lse) if return_lse else o
+
+
+def decode(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
+           softmax_scale: Optional[float] = None, schedule: int = SPLIT,
+           descales=(1.0, 1.0, 1.0), out: Optional[torch.Tensor] = None,
+           return_lse: bool = False, partials: Optional[torch.Tensor] = None, stream=None):
+    """Single-token paged decode; returns O (bf16) and optionally lse."""
+    b, hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty(b, hq, d, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(b, hq, dtype=torch.float32, device=q.device) if return_lse else None
+    if schedule == SPLIT:
+        cmax = attn_num_chunks(max_context_len)
+        part = partials if partials is not None else _new_partials(b, hq, cmax, d, q.device)
+        attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len,
+                              softmax_scale, SPLIT, partials=part, descales=descales,
+                              stream=stream)
+        attn_chunk_merge(part, b, hq, cmax, d, o, lse, v_descale=descales[2], stream=stream)
+    else:
+        attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len,
+                              softmax_scale, MONOLITHIC, o=o, lse=lse, descales=descales,
+                              stream=stream)
+    return (o, lse) if return_lse else o

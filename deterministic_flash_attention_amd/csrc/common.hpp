@@ -1,0 +1,107 @@
+// Shared gfx950 device plumbing: vector types, buffer resource descriptors,
+// LDS helpers and MFMA wrappers.  No attention arithmetic lives here; the
+// numerical contract is in contract.hpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace detattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kWave = 64;
+
+// Raw (stride 0) buffer resource.  Word 3 selects 32-bit data format, the value
+// every gfx9-family raw buffer access uses.  Accesses whose byte offset lies at
+// or beyond num_records read 0 and drop stores; that range check is what bounds
+// every load and store in this library.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_records,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store2(rsrc_t r, uint32_t off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
+// ---- LDS ------------------------------------------------------------------
+__device__ __forceinline__ void lds_store16(unsigned char* lds, uint32_t off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(lds + off) = v;
+}
+__device__ __forceinline__ u32x4 lds_load16(const unsigned char* lds, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(lds + off);
+}
+__device__ __forceinline__ u32x2 lds_load8(const unsigned char* lds, uint32_t off) {
+  return *reinterpret_cast<const u32x2*>(lds + off);
+}
+// gfx950 transposing LDS read: within each 16-lane group, lane i receives
+// element (i % 4) of the 8-byte chunks addressed by lanes (i / 4) + 4r,
+// r = 0..3, in that order.
+__device__ __forceinline__ s16x4 lds_load_tr16(const unsigned char* lds, uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off));
+}
+
+// ---- conversions ----------------------------------------------------------
+// Bits of an fp32 value.  Takes the value by copy: applied directly to an
+// ext-vector element subscript, __builtin_bit_cast reads element 0 instead.
+__device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+}
+// Four OCP E4M3FN codes (one dword) to four bf16 values; exact, since every
+// E4M3FN value is representable in bf16.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  u32x2 r;
+  r[0] = (f32_bits(a[0]) >> 16) | (f32_bits(a[1]) & 0xFFFF0000u);
+  r[1] = (f32_bits(b[0]) >> 16) | (f32_bits(b[1]) & 0xFFFF0000u);
+  return r;
+}
+
+// ---- MFMA -----------------------------------------------------------------
+// v_mfma_f32_32x32x16_{bf16,fp8_fp8}: A is 32x16, lane l supplies
+// A[l % 32][8*(l/32) .. +7]; B is 16x32, lane l supplies B[8*(l/32) .. +7][l % 32];
+// D is 32x32, lane l holds D[8*(i/4) + 4*(l/32) + i%4][l % 32] in element i.
+__device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_fp8(u32x2 a, u32x2 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a),
+                                                    __builtin_bit_cast(long, b), c, 0, 0, 0);
+}
+
+}  // namespace detattn

@@ -1,0 +1,213 @@
+// The numerical contract shared by every kernel of the library.
+//
+// The batch-invariant chunked attention forward (RL-Kernel PR "MFMA
+// batch-invariant GEMM and chunked Triton attention", section 2) requires that
+// prefill, split-KV decode and every batch composition produce bitwise-equal
+// rows.  That holds only if every kernel runs the same fp32 operation sequence
+// per (query row, key block).  This header is that sequence; the prefill,
+// decode and merge kernels call nothing else for arithmetic:
+//
+//   * keys are consumed in 64-key blocks at absolute positions inside 512-key
+//     chunks; each chunk's online softmax starts from the empty state
+//     (m = -inf, l = 0, acc = 0);
+//   * S^T = K Q^T per block on v_mfma_f32_32x32x16 (bf16, or fp8 for e4m3
+//     inputs), D/16 K-steps in ascending order from a zero accumulator; the
+//     instruction shape and the K order are part of the contract, as the same
+//     page says of its GEMM sibling (section 1);
+//   * scores are multiplied once by c = scale * q_descale * k_descale * log2(e)
+//     and masked by select, never by adding;
+//   * row max over the block (exact in any order), then
+//     alpha = exp2(m - m'), p = exp2(s - m') with v_exp_f32, a fixed row-sum
+//     tree, l = l*alpha + sum(p); a row whose block is fully masked keeps
+//     m, l and acc bit for bit (alpha = 1, p = 0, and its empty state uses the
+//     safe max 0 so no -inf - -inf appears);
+//   * P is rounded to bf16 (nearest even) and acc = (acc*alpha) + P V on
+//     v_mfma_f32_32x32x16_bf16, four 16-key K-steps in ascending key order; fp8
+//     V is widened exactly to bf16 first;
+//   * chunk partials (m_c, l_c, acc_c) are folded left to right in ascending
+//     chunk order with the exact max/sum rescale (a skipped empty partial, a
+//     copy into an empty total, or M' = max(M, m_c), a = exp2(M - M'),
+//     b = exp2(m_c - M'), L = L*a + l_c*b, A = A*a + acc_c*b);
+//   * O = L > 0 ? A / L : 0 (IEEE division) times v_descale, rounded once to bf16.
+//
+// All code is built with -ffp-contract=off: no multiply-add is fused, so each
+// product and sum above is a separately rounded fp32 operation in every kernel.
+#pragma once
+
+#include "common.hpp"
+
+namespace detattn {
+
+constexpr int kBlockKeys = 64;
+constexpr int kChunkKeys = 512;
+constexpr int kBlocksPerChunk = kChunkKeys / kBlockKeys;
+constexpr uint32_t kParked = 0x80000000u;  // store offset past every num_records
+
+template <int D, bool FP8>
+struct Geom {
+  static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim must be a multiple of 32");
+  static constexpr int kEs = FP8 ? 1 : 2;       // bytes per Q/K/V element in HBM
+  static constexpr int kRowBytes = D * kEs;     // one head row of Q/K/V
+  static constexpr int kQRow = kRowBytes + 16;  // LDS row strides (padded by 16 B)
+  static constexpr int kKRow = kRowBytes + 16;
+  static constexpr int kVRow = D * 2 + 16;      // V is staged as bf16
+  static constexpr int kKStage = kBlockKeys * kKRow;
+  static constexpr int kVStage = kBlockKeys * kVRow;
+  static constexpr int kSteps = D / 16;         // QK^T K-steps
+  static constexpr int kDTiles = D / 32;        // 32-wide output tiles for PV
+  static constexpr int kChunks16 = kRowBytes / 16;  // 16-byte chunks per HBM row
+};
+
+// Q^T operand of one K-step: 8 bf16 (16 bytes) or 8 e4m3 (8 bytes) per lane.
+template <bool FP8> struct QFrag { u32x4 v; };
+template <> struct QFrag<true> { u32x2 v; };
+
+// Score element i of key tile t in lane (n, h = lane/32) is the key at offset
+// 32t + 16(i/8) + 8h + (i%8) of the block: MFMA row r of tile t holds key
+// 32t + sigma(r), sigma swapping bits 2 and 3 of r, so that each lane holds 8
+// consecutive keys per 16-key PV step and P feeds the PV MFMA with no lane
+// exchange.
+__device__ __forceinline__ int key_sigma(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+__device__ __forceinline__ int score_key(int t, int i, int h) {
+  return 32 * t + 16 * (i >> 3) + 8 * h + (i & 7);
+}
+
+// S^T = K_blk Q^T for the 64 keys of the staged block; s[t] holds key tile t.
+template <int D, bool FP8>
+__device__ __forceinline__ void qk_scores(f32x16 (&s)[2], const QFrag<FP8> (&q)[D / 16],
+                                          const unsigned char* ks, int lane) {
+  using G = Geom<D, FP8>;
+  const int row = key_sigma(lane & 31);
+  const int h = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < G::kSteps; ++st) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t off = (uint32_t)((32 * t + row) * G::kKRow + (16 * st + 8 * h) * G::kEs);
+      if constexpr (FP8) {
+        s[t] = mfma_fp8(lds_load8(ks, off), q[st].v, s[t]);
+      } else {
+        s[t] = mfma_bf16(lds_load16(ks, off), q[st].v, s[t]);
+      }
+    }
+  }
+}
+
+// Online-softmax update of one lane's query column over a 64-key block.
+// rel_lim: keys at block offset >= rel_lim are masked (MASKED only).
+// Returns alpha for the accumulator and P^T as four bf16x8 PV operands.
+template <bool MASKED>
+__device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float c, int rel_lim,
+                                              float& m, float& l, float& alpha,
+                                              u32x4 (&pb)[4]) {
+  float x[2][16];
+  float mb = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float v = s[t][i] * c;
+      if constexpr (MASKED) v = (score_key(t, i, h) < rel_lim) ? v : -INFINITY;
+      x[t][i] = v;
+      mb = fmaxf(mb, v);
+    }
+  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  const float mn = fmaxf(m, mb);
+  const bool empty = (mn == -INFINITY);
+  const float msafe = empty ? 0.0f : mn;
+  alpha = empty ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+  float p[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[t][i] = __builtin_amdgcn_exp2f(x[t][i] - msafe);
+  // Row-sum tree: pair the two key tiles, then halve 16 -> 1, then add the
+  // other half-wave (lane ^ 32), which holds the remaining 32 keys.
+  float u[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) u[i] = p[0][i] + p[1][i];
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) u[i] = u[i] + u[i + w];
+  const float rs = u[0] + __shfl_xor(u[0], 32);
+  l = l * alpha + rs;
+  m = mn;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int t = kk >> 1, b = 8 * (kk & 1);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pb[kk][e] = pack_bf16x2(p[t][b + 2 * e], p[t][b + 2 * e + 1]);
+  }
+}
+
+// acc_j = acc_j * alpha + P V for the NT output tiles starting at tile dt0.
+// The V^T operand comes from the row-major bf16 V stage through the transposing
+// LDS read: lane (group G, i) gets V[16kk + 8h + 0..7][32dt + 16(G%2) + i].
+template <int D, int NT>
+__device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[NT], int dt0, float alpha,
+                                              const u32x4 (&pb)[4], const unsigned char* vs,
+                                              int lane) {
+  constexpr int kVRow = D * 2 + 16;
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[j][i] = acc[j][i] * alpha;
+  const int grp = lane >> 4, li = lane & 15;
+  const int h = grp >> 1;
+  const int key_r = li >> 2, dq = (li & 3) * 4;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int d = 32 * (dt0 + j) + 16 * (grp & 1) + dq;
+      const uint32_t off0 = (uint32_t)((16 * kk + 8 * h + key_r) * kVRow + d * 2);
+      const s16x4 lo = lds_load_tr16(vs, off0);
+      const s16x4 hi = lds_load_tr16(vs, off0 + 4 * kVRow);
+      u32x4 a;
+      a[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+      a[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+      a[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+      a[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+      acc[j] = mfma_bf16(a, pb[kk], acc[j]);
+    }
+  }
+}
+
+// Chunk merge: fold one partial (m, l) into the running (M, L).
+// mode 0: partial empty, keep; 1: total empty, copy; 2: rescale with (ca, cb).
+__device__ __forceinline__ void merge_stats(float& M, float& L, float m, float l, float& ca,
+                                            float& cb, int& mode) {
+  const bool part_empty = (m == -INFINITY);
+  const bool tot_empty = (M == -INFINITY);
+  const float Mn = fmaxf(M, m);
+  const float a = __builtin_amdgcn_exp2f(M - Mn);
+  const float b = __builtin_amdgcn_exp2f(m - Mn);
+  mode = part_empty ? 0 : (tot_empty ? 1 : 2);
+  ca = a;
+  cb = b;
+  const float Lr = L * a + l * b;
+  L = (mode == 0) ? L : ((mode == 1) ? l : Lr);
+  M = (mode == 0) ? M : ((mode == 1) ? m : Mn);
+}
+__device__ __forceinline__ float merge_elem(float A, float acc, int mode, float ca, float cb) {
+  const float r = A * ca + acc * cb;
+  return (mode == 0) ? A : ((mode == 1) ? acc : r);
+}
+
+__device__ __forceinline__ float finalize_elem(float A, float L, float v_descale) {
+  const float o = (L > 0.0f) ? (A / L) : 0.0f;
+  return o * v_descale;
+}
+// Natural-log sum of exp(scale * q.k): M is kept in log2 units.
+__device__ __forceinline__ float finalize_lse(float M, float L) {
+  return (L > 0.0f) ? (M + __builtin_amdgcn_logf(L)) * 0.693147180559945309f : -INFINITY;
+}
+
+}  // namespace detattn

@@ -1,0 +1,268 @@
+// Single-token paged decode over a paged KV cache (page size 16).
+//
+// Split schedule (RL-Kernel page, section 2: one program per sequence / KV
+// head / chunk, then a merge): one workgroup per (sequence, kv-head, 512-key
+// chunk) folds its chunk from the empty state for the query heads of the
+// kv-head's group and stores the fp32 partial; the merge kernel folds the
+// partials in ascending chunk order.  The monolithic schedule folds every chunk
+// of a (sequence, kv-head) in registers and stores O; it exists so that tests
+// can check that the two schedules agree bit for bit.
+//
+// The query heads of one group occupy columns 0..G-1 of the 32-column MFMA
+// tile; the remaining columns carry zero queries and are never stored.  Every
+// wave computes the (identical) scores and softmax for all columns and owns one
+// 32-wide slice of the output, so D/32 waves share the K/V traffic of a block.
+// The per-block arithmetic is the one in contract.hpp, which makes a decode row
+// bitwise equal to the last row of the prefill of the same sequence.
+#include "contract.hpp"
+#include "kernels.hpp"
+
+namespace detattn {
+
+namespace {
+
+constexpr int kPageSize = 16;
+
+template <int D, bool FP8>
+struct DecodeCfg {
+  using G = Geom<D, FP8>;
+  static constexpr int kWaves = D / 32;
+  static constexpr int kThreads = kWaves * kWave;
+  static constexpr int kBlockChunks = kBlockKeys * G::kChunks16;
+  static constexpr int kPerThread = kBlockChunks / kThreads;
+  static_assert(kPerThread * kThreads == kBlockChunks, "K/V chunks must split evenly");
+  static constexpr int kKOff = 0;
+  static constexpr int kVOff = 2 * G::kKStage;
+  static constexpr int kLds = kVOff + 2 * G::kVStage;
+  static_assert(kLds <= 160 * 1024, "LDS budget");
+};
+
+template <int D, bool FP8>
+struct PagedStager {
+  using G = Geom<D, FP8>;
+  using C = DecodeCfg<D, FP8>;
+  u32x4 kreg[C::kPerThread];
+  u32x4 vreg[C::kPerThread];
+
+  // Keys at or past ctx, and keys whose page index is outside the cache, are
+  // staged as zeros, so dead slots (whatever they hold) never reach the MFMA.
+  __device__ __forceinline__ void load(const DecodeParams& p, const unsigned char* kc,
+                                       const unsigned char* vc, const int32_t* table, int key0,
+                                       int ctx, int64_t head_off, int tid) {
+#pragma unroll
+    for (int u = 0; u < C::kPerThread; ++u) {
+      const int x = tid + u * C::kThreads;
+      const int r = x / G::kChunks16, col = x % G::kChunks16;
+      const int j = key0 + r;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (j < ctx) {
+        const int64_t page = table[j / kPageSize];
+        if (page >= 0 && page < p.num_pages) {
+          const int64_t e = page * p.page_stride + (int64_t)(j % kPageSize) * p.token_stride + head_off;
+          const int64_t byte = e * G::kEs + (int64_t)col * 16;
+          kv = *reinterpret_cast<const u32x4*>(kc + byte);
+          vv = *reinterpret_cast<const u32x4*>(vc + byte);
+        }
+      }
+      kreg[u] = kv;
+      vreg[u] = vv;
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* ks, unsigned char* vs, int tid) const {
+#pragma unroll
+    for (int u = 0; u < C::kPerThread; ++u) {
+      const int x = tid + u * C::kThreads;
+      const int r = x / G::kChunks16, col = x % G::kChunks16;
+      lds_store16(ks, (uint32_t)(r * G::kKRow + col * 16), kreg[u]);
+      if constexpr (FP8) {
+        const u32x2 a = e4m3x4_to_bf16x4(vreg[u][0]), b = e4m3x4_to_bf16x4(vreg[u][1]);
+        const u32x2 c = e4m3x4_to_bf16x4(vreg[u][2]), d = e4m3x4_to_bf16x4(vreg[u][3]);
+        const uint32_t o = (uint32_t)(r * G::kVRow + col * 32);
+        lds_store16(vs, o, u32x4{a[0], a[1], b[0], b[1]});
+        lds_store16(vs, o + 16, u32x4{c[0], c[1], d[0], d[1]});
+      } else {
+        lds_store16(vs, (uint32_t)(r * G::kVRow + col * 16), vreg[u]);
+      }
+    }
+  }
+};
+
+template <int D, bool FP8, bool SPLIT>
+__global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams p) {
+  using G = Geom<D, FP8>;
+  using C = DecodeCfg<D, FP8>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
+  unsigned char* const sK = smem + C::kKOff;
+  unsigned char* const sV = smem + C::kVOff;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, n = lane & 31;
+  int id = blockIdx.x;
+  int chunk = 0;
+  if constexpr (SPLIT) {
+    chunk = id % p.cmax;
+    id /= p.cmax;
+  }
+  const int g = id % p.hkv;
+  const int b = id / p.hkv;
+  const int grp = p.group;
+
+  int ctx = uniform(p.ctx_lens[b]);
+  ctx = max(0, min(ctx, p.max_pages * kPageSize));
+  const int nblk = (ctx + kBlockKeys - 1) / kBlockKeys;
+  int blk_begin = 0, blk_end = nblk;
+  if constexpr (SPLIT) {
+    blk_begin = chunk * kBlocksPerChunk;
+    blk_end = min(blk_begin + kBlocksPerChunk, nblk);
+  }
+
+  const int64_t row_head = (int64_t)b * p.hq + (int64_t)g * grp;  // first query head of the group
+  const bool ml_writer = (wave == 0) && (h == 0);
+
+  if constexpr (SPLIT) {
+    if (blk_begin >= blk_end) {
+      const int64_t mlh = (int64_t)chunk * p.batch * p.hq + row_head;
+      const rsrc_t mlr = make_rsrc(p.part_ml + 2 * mlh, (uint32_t)grp * 8u);
+      buf_store8(mlr, ml_writer ? (uint32_t)n * 8u : kParked,
+                 u32x2{f32_bits(-INFINITY), 0u});
+      return;
+    }
+  }
+
+  // Q^T operands straight from HBM; columns >= G read zero (descriptor bound).
+  QFrag<FP8> qf[G::kSteps];
+  {
+    const rsrc_t qr = make_rsrc(static_cast<const unsigned char*>(p.q) + row_head * G::kRowBytes,
+                                (uint32_t)(grp * G::kRowBytes));
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) {
+      const uint32_t off = (uint32_t)(n * G::kRowBytes + (16 * st + 8 * h) * G::kEs);
+      if constexpr (FP8) {
+        qf[st].v = buf_load8(qr, off);
+      } else {
+        qf[st].v = buf_load16(qr, off);
+      }
+    }
+  }
+
+  const float c = p.c_scale;
+  f32x16 acc[1], A[1];
+  float m = -INFINITY, l = 0.0f, M = -INFINITY, L = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    acc[0][i] = 0.0f;
+    A[0][i] = 0.0f;
+  }
+
+  if (blk_begin < blk_end) {
+    const unsigned char* kc = static_cast<const unsigned char*>(p.kc);
+    const unsigned char* vc = static_cast<const unsigned char*>(p.vc);
+    const int32_t* table = p.page_table + (int64_t)b * p.max_pages;
+    const int64_t head_off = (int64_t)g * p.head_stride;
+    PagedStager<D, FP8> stg;
+    stg.load(p, kc, vc, table, blk_begin * kBlockKeys, ctx, head_off, tid);
+    stg.store(sK, sV, tid);
+    __syncthreads();
+    for (int blk = blk_begin; blk < blk_end; ++blk) {
+      const int cur = (blk - blk_begin) & 1;
+      const bool more = blk + 1 < blk_end;
+      if (more) stg.load(p, kc, vc, table, (blk + 1) * kBlockKeys, ctx, head_off, tid);
+      const unsigned char* ks = sK + cur * G::kKStage;
+      const unsigned char* vs = sV + cur * G::kVStage;
+      f32x16 s[2];
+      qk_scores<D, FP8>(s, qf, ks, lane);
+      float alpha;
+      u32x4 pb[4];
+      if (kBlockKeys * (blk + 1) <= ctx) {
+        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+      } else {
+        softmax_block<true>(s, h, c, ctx - kBlockKeys * blk, m, l, alpha, pb);
+      }
+      pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
+      if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
+      __syncthreads();
+      if constexpr (!SPLIT) {
+        if (((blk + 1) % kBlocksPerChunk) == 0 || !more) {
+          float ca, cb;
+          int mode;
+          merge_stats(M, L, m, l, ca, cb, mode);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            A[0][i] = merge_elem(A[0][i], acc[0][i], mode, ca, cb);
+            acc[0][i] = 0.0f;
+          }
+          m = -INFINITY;
+          l = 0.0f;
+        }
+      }
+    }
+  }
+
+  if constexpr (SPLIT) {
+    const int64_t mlh = (int64_t)chunk * p.batch * p.hq + row_head;
+    const rsrc_t mlr = make_rsrc(p.part_ml + 2 * mlh, (uint32_t)grp * 8u);
+    buf_store8(mlr, ml_writer ? (uint32_t)n * 8u : kParked,
+               u32x2{f32_bits(m), f32_bits(l)});
+    const rsrc_t ar = make_rsrc(p.part_acc + mlh * D, (uint32_t)grp * D * 4u);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * wave + 8 * q4 + 4 * h;
+      buf_store16(ar, (uint32_t)(n * D + d) * 4u,
+                  u32x4{f32_bits(acc[0][4 * q4 + 0]),
+                        f32_bits(acc[0][4 * q4 + 1]),
+                        f32_bits(acc[0][4 * q4 + 2]),
+                        f32_bits(acc[0][4 * q4 + 3])});
+    }
+  } else {
+    const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + row_head * D * 2,
+                                 (uint32_t)grp * D * 2u);
+    const float vd = p.v_descale;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * wave + 8 * q4 + 4 * h;
+      const uint32_t w0 = pack_bf16x2(finalize_elem(A[0][4 * q4 + 0], L, vd),
+                                      finalize_elem(A[0][4 * q4 + 1], L, vd));
+      const uint32_t w1 = pack_bf16x2(finalize_elem(A[0][4 * q4 + 2], L, vd),
+                                      finalize_elem(A[0][4 * q4 + 3], L, vd));
+      buf_store8(orr, (uint32_t)(n * D + d) * 2u, u32x2{w0, w1});
+    }
+    if (p.lse != nullptr) {
+      const rsrc_t lr = make_rsrc(p.lse + row_head, (uint32_t)grp * 4u);
+      buf_store4(lr, ml_writer ? (uint32_t)n * 4u : kParked,
+                 f32_bits(finalize_lse(M, L)));
+    }
+  }
+}
+
+template <int D, bool FP8>
+hipError_t launch_one(const DecodeParams& p, bool split, hipStream_t stream) {
+  const long long per = (long long)p.batch * p.hkv * (split ? p.cmax : 1);
+  if (per <= 0) return hipSuccess;
+  dim3 grid((unsigned)per), block(DecodeCfg<D, FP8>::kThreads);
+  if (split) {
+    hipLaunchKernelGGL((decode_kernel<D, FP8, true>), grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<D, FP8, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool split,
+                         hipStream_t stream) {
+  switch (head_dim) {
+    case 64:
+      return fp8 ? launch_one<64, true>(p, split, stream) : launch_one<64, false>(p, split, stream);
+    case 128:
+      return fp8 ? launch_one<128, true>(p, split, stream)
+                 : launch_one<128, false>(p, split, stream);
+    case 192:
+      return fp8 ? launch_one<192, true>(p, split, stream)
+                 : launch_one<192, false>(p, split, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace detattn

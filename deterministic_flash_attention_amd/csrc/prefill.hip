@@ -1,0 +1,336 @@
+// Prefill / full-sequence forward over packed variable-length sequences.
+//
+// One workgroup owns a tile of 32*NW query rows of one (sequence, query head).
+// The Q tile is staged once in its own LDS region and each wave keeps its 32
+// rows' Q^T operands in registers; K and V blocks of 64 keys stream through
+// two LDS stages that are disjoint from the Q region (the ffpa-attn fp8 D=192
+// page shows what a K stage landing in a live Q tile does).  Keys are folded in
+// 512-key chunks exactly as contract.hpp prescribes.
+//
+// Schedules (RL-Kernel page, section 2):
+//   monolithic  the workgroup folds every chunk of its tile in registers and
+//               stores bf16 O (and lse);
+//   split       one workgroup per (tile, head, chunk) stores the fp32 chunk
+//               partial; the merge kernel folds the partials.  Both run the
+//               same per-chunk code, so the merged result is bit-identical.
+//
+// Stores are bounded by buffer descriptors whose num_records ends at the last
+// valid row of the sequence (FlyDSL conv3d and aiter MQA-logits pages): padded
+// tail rows of a tile are dropped by the hardware range check, so they can
+// never land on the next sequence's rows.
+#include "contract.hpp"
+#include "kernels.hpp"
+
+namespace detattn {
+
+namespace {
+
+template <int D, bool FP8, int NW>
+struct PrefillCfg {
+  using G = Geom<D, FP8>;
+  static constexpr int kThreads = NW * kWave;
+  static constexpr int kTileRows = 32 * NW;
+  static constexpr int kQBytes = kTileRows * G::kQRow;
+  static constexpr int kBlockChunks = kBlockKeys * G::kChunks16;  // 16-B chunks per K block
+  static constexpr int kPerThread = (kBlockChunks + kThreads - 1) / kThreads;
+  static constexpr int kKOff = kQBytes;
+  static constexpr int kVOff = kKOff + 2 * G::kKStage;
+  static constexpr int kLds = kVOff + 2 * G::kVStage;
+  // Q tile, the two K stages and the two V stages are disjoint byte ranges.
+  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * G::kKStage, "LDS regions overlap");
+  static_assert(kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
+};
+
+__device__ __forceinline__ uint32_t extent_bytes(int64_t nrows, int64_t row_bytes,
+                                                 int64_t width_bytes, int64_t avail) {
+  if (nrows <= 0 || avail <= 0) return 0u;
+  int64_t e = (nrows - 1) * row_bytes + width_bytes;
+  if (e > avail) e = avail;
+  if (e > 0x7FFFFFFF) e = 0x7FFFFFFF;
+  return (uint32_t)e;
+}
+
+// Global -> registers -> LDS staging of one 64-key K and V block.
+template <int D, bool FP8, int NW>
+struct KVStager {
+  using G = Geom<D, FP8>;
+  using C = PrefillCfg<D, FP8, NW>;
+  u32x4 kreg[C::kPerThread];
+  u32x4 vreg[C::kPerThread];
+
+  __device__ __forceinline__ void load(rsrc_t kr, rsrc_t vr, int key0, uint32_t row_bytes,
+                                       int tid) {
+#pragma unroll
+    for (int u = 0; u < C::kPerThread; ++u) {
+      const int x = tid + u * C::kThreads;
+      if (C::kPerThread * C::kThreads == C::kBlockChunks || x < C::kBlockChunks) {
+        const int r = x / G::kChunks16, col = x % G::kChunks16;
+        const uint32_t off = (uint32_t)(key0 + r) * row_bytes + (uint32_t)col * 16u;
+        kreg[u] = buf_load16(kr, off);
+        vreg[u] = buf_load16(vr, off);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(unsigned char* ks, unsigned char* vs, int tid) const {
+#pragma unroll
+    for (int u = 0; u < C::kPerThread; ++u) {
+      const int x = tid + u * C::kThreads;
+      if (C::kPerThread * C::kThreads == C::kBlockChunks || x < C::kBlockChunks) {
+        const int r = x / G::kChunks16, col = x % G::kChunks16;
+        lds_store16(ks, (uint32_t)(r * G::kKRow + col * 16), kreg[u]);
+        if constexpr (FP8) {
+          const u32x2 a = e4m3x4_to_bf16x4(vreg[u][0]), b = e4m3x4_to_bf16x4(vreg[u][1]);
+          const u32x2 c = e4m3x4_to_bf16x4(vreg[u][2]), d = e4m3x4_to_bf16x4(vreg[u][3]);
+          const uint32_t o = (uint32_t)(r * G::kVRow + col * 32);
+          lds_store16(vs, o, u32x4{a[0], a[1], b[0], b[1]});
+          lds_store16(vs, o + 16, u32x4{c[0], c[1], d[0], d[1]});
+        } else {
+          lds_store16(vs, (uint32_t)(r * G::kVRow + col * 16), vreg[u]);
+        }
+      }
+    }
+  }
+};
+
+template <int D, bool FP8, int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p) {
+  using G = Geom<D, FP8>;
+  using C = PrefillCfg<D, FP8, NW>;
+  constexpr int NT = G::kDTiles;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
+  unsigned char* const sQ = smem;
+  unsigned char* const sK = smem + C::kKOff;
+  unsigned char* const sV = smem + C::kVOff;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5;
+  // Work decode: batch fastest, then head, then (split) chunk, then tiles from
+  // the last (heaviest under a causal mask) to the first.
+  int id = blockIdx.x;
+  const int b = id % p.batch;
+  id /= p.batch;
+  const int head = id % p.hq;
+  id /= p.hq;
+  int chunk = 0;
+  if constexpr (SPLIT) {
+    chunk = id % p.cmax;
+    id /= p.cmax;
+  }
+  const int tile_rev = id;
+
+  const int q_start = uniform(p.cu_q[b]);
+  const int lq = uniform(p.cu_q[b + 1]) - q_start;
+  const int k_start = uniform(p.cu_k[b]);
+  const int lk = uniform(p.cu_k[b + 1]) - k_start;
+  if (lq <= 0 || q_start < 0 || k_start < 0) return;
+  const int ntiles = (lq + C::kTileRows - 1) / C::kTileRows;
+  const int tile = ntiles - 1 - tile_rev;
+  if (tile < 0) return;
+  const int r0 = tile * C::kTileRows;
+  const int g = head / (p.hq / p.hkv);
+
+  // Key ranges of this tile (bottom-right causal alignment).
+  const int koff = lk - lq;
+  const int last = min(r0 + C::kTileRows, lq) - 1;
+  const int kend = p.causal ? min(lk, last + koff + 1) : lk;  // visible to some real row
+  const int kfull = p.causal ? min(lk, r0 + koff + 1) : lk;   // visible to every real row
+  const int nblk = kend > 0 ? (kend + kBlockKeys - 1) / kBlockKeys : 0;
+  int blk_begin = 0, blk_end = nblk;
+  if constexpr (SPLIT) {
+    blk_begin = chunk * kBlocksPerChunk;
+    blk_end = min(blk_begin + kBlocksPerChunk, nblk);
+  }
+
+  const int qrow = r0 + 32 * wave + (lane & 31);  // local query row of this lane
+  const int lim = p.causal ? min(lk, qrow + koff + 1) : lk;
+
+  if constexpr (SPLIT) {
+    if (blk_begin >= blk_end) {
+      // Empty chunk for this tile: every row's partial is (m, l) = (-inf, 0).
+      const int64_t ml_head = ((int64_t)chunk * p.total_q + q_start) * p.hq + head;
+      const rsrc_t mlr = make_rsrc(p.part_ml + 2 * ml_head,
+                                   extent_bytes(lq, (int64_t)p.hq * 8, 8,
+                                                ((int64_t)(chunk + 1) * p.total_q * p.hq - ml_head) * 8));
+      const uint32_t off = h ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 8);
+      buf_store8(mlr, off, u32x2{f32_bits(-INFINITY), 0u});
+      return;
+    }
+  }
+
+  const float c = p.c_scale;
+  f32x16 acc[NT];
+  f32x16 A[NT];
+  float m = -INFINITY, l = 0.0f, M = -INFINITY, L = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acc[j][i] = 0.0f;
+      A[j][i] = 0.0f;
+    }
+
+  if (blk_begin < blk_end) {
+    const int64_t q_head = (int64_t)q_start * p.hq + head;
+    const int64_t kv_head = (int64_t)k_start * p.hkv + g;
+    const uint32_t q_row_bytes = (uint32_t)(p.hq * G::kRowBytes);
+    const uint32_t kv_row_bytes = (uint32_t)(p.hkv * G::kRowBytes);
+    const unsigned char* qb = static_cast<const unsigned char*>(p.q) + q_head * G::kRowBytes;
+    const unsigned char* kb = static_cast<const unsigned char*>(p.k) + kv_head * G::kRowBytes;
+    const unsigned char* vb = static_cast<const unsigned char*>(p.v) + kv_head * G::kRowBytes;
+    const rsrc_t qr = make_rsrc(qb, extent_bytes(lq, q_row_bytes, G::kRowBytes,
+                                                 (p.total_q * p.hq - q_head) * G::kRowBytes));
+    const uint32_t kv_ext = extent_bytes(lk, kv_row_bytes, G::kRowBytes,
+                                         (p.total_k * p.hkv - kv_head) * G::kRowBytes);
+    const rsrc_t kr = make_rsrc(kb, kv_ext);
+    const rsrc_t vr = make_rsrc(vb, kv_ext);
+
+    KVStager<D, FP8, NW> stg;
+    stg.load(kr, vr, blk_begin * kBlockKeys, kv_row_bytes, tid);
+    // Q tile -> LDS (rows past the sequence read as zero).
+    for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
+      const int r = x / G::kChunks16, col = x % G::kChunks16;
+      lds_store16(sQ, (uint32_t)(r * G::kQRow + col * 16),
+                  buf_load16(qr, (uint32_t)(r0 + r) * q_row_bytes + (uint32_t)col * 16u));
+    }
+    stg.store(sK, sV, tid);
+    __syncthreads();
+
+    QFrag<FP8> qf[G::kSteps];
+    {
+      const int row = 32 * wave + (lane & 31);
+#pragma unroll
+      for (int st = 0; st < G::kSteps; ++st) {
+        const uint32_t off = (uint32_t)(row * G::kQRow + (16 * st + 8 * h) * G::kEs);
+        if constexpr (FP8) {
+          qf[st].v = lds_load8(sQ, off);
+        } else {
+          qf[st].v = lds_load16(sQ, off);
+        }
+      }
+    }
+
+    for (int blk = blk_begin; blk < blk_end; ++blk) {
+      const int cur = (blk - blk_begin) & 1;
+      const bool more = blk + 1 < blk_end;
+      if (more) stg.load(kr, vr, (blk + 1) * kBlockKeys, kv_row_bytes, tid);
+      const unsigned char* ks = sK + cur * G::kKStage;
+      const unsigned char* vs = sV + cur * G::kVStage;
+      f32x16 s[2];
+      qk_scores<D, FP8>(s, qf, ks, lane);
+      float alpha;
+      u32x4 pb[4];
+      if (kBlockKeys * (blk + 1) <= kfull) {
+        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+      } else {
+        softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
+      }
+      pv_accumulate<D, NT>(acc, 0, alpha, pb, vs, lane);
+      if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
+      __syncthreads();
+      if constexpr (!SPLIT) {
+        if (((blk + 1) % kBlocksPerChunk) == 0 || !more) {
+          float ca, cb;
+          int mode;
+          merge_stats(M, L, m, l, ca, cb, mode);
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              A[j][i] = merge_elem(A[j][i], acc[j][i], mode, ca, cb);
+              acc[j][i] = 0.0f;
+            }
+          m = -INFINITY;
+          l = 0.0f;
+        }
+      }
+    }
+  }
+
+  if constexpr (SPLIT) {
+    const int64_t ml_head = ((int64_t)chunk * p.total_q + q_start) * p.hq + head;
+    const rsrc_t mlr = make_rsrc(p.part_ml + 2 * ml_head,
+                                 extent_bytes(lq, (int64_t)p.hq * 8, 8,
+                                              ((int64_t)(chunk + 1) * p.total_q * p.hq - ml_head) * 8));
+    buf_store8(mlr, h ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 8),
+               u32x2{f32_bits(m), f32_bits(l)});
+    const int64_t acc_head = ml_head * D;
+    const rsrc_t ar = make_rsrc(p.part_acc + acc_head,
+                                extent_bytes(lq, (int64_t)p.hq * D * 4, D * 4,
+                                             ((int64_t)(chunk + 1) * p.total_q * p.hq * D - acc_head) * 4));
+    const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(p.hq * D * 4);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * j + 8 * q4 + 4 * h;
+        buf_store16(ar, rowoff + (uint32_t)d * 4u,
+                    u32x4{f32_bits(acc[j][4 * q4 + 0]),
+                          f32_bits(acc[j][4 * q4 + 1]),
+                          f32_bits(acc[j][4 * q4 + 2]),
+                          f32_bits(acc[j][4 * q4 + 3])});
+      }
+  } else {
+    const int64_t o_head = (int64_t)q_start * p.hq + head;
+    const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + o_head * D * 2,
+                                 extent_bytes(lq, (int64_t)p.hq * D * 2, D * 2,
+                                              (p.total_q * p.hq - o_head) * D * 2));
+    const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(p.hq * D * 2);
+    const float vd = p.v_descale;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * j + 8 * q4 + 4 * h;
+        const uint32_t w0 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 0], L, vd),
+                                        finalize_elem(A[j][4 * q4 + 1], L, vd));
+        const uint32_t w1 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 2], L, vd),
+                                        finalize_elem(A[j][4 * q4 + 3], L, vd));
+        buf_store8(orr, rowoff + (uint32_t)d * 2u, u32x2{w0, w1});
+      }
+    if (p.lse != nullptr) {
+      const rsrc_t lr = make_rsrc(p.lse + o_head, extent_bytes(lq, (int64_t)p.hq * 4, 4,
+                                                               (p.total_q * p.hq - o_head) * 4));
+      buf_store4(lr, h ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 4),
+                 f32_bits(finalize_lse(M, L)));
+    }
+  }
+}
+
+template <int D, bool FP8, int NW>
+hipError_t launch_one(const PrefillParams& p, bool split, hipStream_t stream) {
+  const long long per = (long long)p.batch * p.hq * p.tiles * (split ? p.cmax : 1);
+  if (per <= 0) return hipSuccess;
+  dim3 grid((unsigned)per), block(NW * kWave);
+  if (split) {
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, true>), grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+constexpr int kPrefillWaves = 4;
+
+}  // namespace
+
+int prefill_tile_rows(int, bool) { return 32 * kPrefillWaves; }
+
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, bool split,
+                          hipStream_t stream) {
+  constexpr int NW = kPrefillWaves;
+  switch (head_dim) {
+    case 64:
+      return fp8 ? launch_one<64, true, NW>(p, split, stream)
+                 : launch_one<64, false, NW>(p, split, stream);
+    case 128:
+      return fp8 ? launch_one<128, true, NW>(p, split, stream)
+                 : launch_one<128, false, NW>(p, split, stream);
+    case 192:
+      return fp8 ? launch_one<192, true, NW>(p, split, stream)
+                 : launch_one<192, false, NW>(p, split, stream);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace detattn

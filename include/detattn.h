@@ -1,0 +1,162 @@
+/*
+ * detattn — batch-invariant chunked flash-attention forward for MI355X (gfx950).
+ *
+ * The operation (RL-Kernel PR "MFMA batch-invariant GEMM and chunked Triton
+ * attention", section 2 "Chunked-KV Triton flash attention") is
+ *
+ *     O = softmax(scale * Q K^T + mask) V
+ *
+ * served by one arithmetic path for full-sequence forward, prefill,
+ * prefix-cached extend and single-token paged decode: keys are consumed in
+ * 64-key blocks inside 512-key chunks, each chunk's online softmax starts from
+ * an empty state, chunk partials are merged in ascending order with the exact
+ * max/sum rescale, fully masked blocks leave a row untouched, and no
+ * multiply-add is fused.  A monolithic schedule (one workgroup per query tile)
+ * and a split schedule (one workgroup per sequence / head / chunk, then
+ * attn_chunk_merge) give bit-identical rows, so a decode row equals the last row
+ * of the prefill of the same sequence, and a row does not depend on which other
+ * sequences share the batch.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are caller-owned device memory, row-major and contiguous
+ *     unless strides are given.  The library allocates nothing, keeps no state,
+ *     never synchronises the host and launches only on `stream` (a hipStream_t;
+ *     NULL is the null stream).  Calls on different streams may run concurrently.
+ *   - Mask: key j of a sequence with L_q queries and L_k keys is visible from
+ *     query row i iff j < L_k and (causal == 0 or j <= i + L_k - L_q), i.e.
+ *     causal masks are aligned to the bottom-right corner.  A row with no
+ *     visible key gets O = 0 and lse = -inf.
+ *   - Grouped-query attention: query head h reads kv head h / (Hq / Hkv).
+ *   - dtype DA_BF16: Q, K, V are bf16, all descales must be 1.0f.
+ *     dtype DA_FP8_E4M3: Q, K, V are OCP E4M3FN codes with per-tensor fp32
+ *     dequantisation scales (value = code * descale); scores use
+ *     scale * q_descale * k_descale, P V runs in bf16 on exactly widened V, and
+ *     the output is multiplied by v_descale.  O is always bf16.
+ *   - lse (optional, may be NULL) is fp32, the natural log of
+ *     sum_j exp(scale * q.k_j) over visible keys.
+ *   - Stores never leave the valid cells: padded rows of a tile, rows of other
+ *     sequences and cells outside [0, D) are not written, so whatever the caller
+ *     pre-filled elsewhere in O survives.
+ *   - Errors: arguments are checked on the host before anything is launched; a
+ *     failing check returns its status with nothing launched and nothing
+ *     written.  DA_ELAUNCH reports a launch failure.  Device-side values
+ *     (cu_seqlens, context_lens, page tables) are not checked on the host; the
+ *     kernels clamp every access to the extents passed here, so malformed
+ *     values cannot read or write outside the given tensors.
+ */
+#ifndef DETATTN_H
+#define DETATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DA_OK = 0,
+  DA_EINVAL = 1,       /* malformed argument (null pointer, bad count, misalignment) */
+  DA_EUNSUPPORTED = 2, /* well-formed but outside what the kernels implement */
+  DA_EWORKSPACE = 3,   /* partials buffer too small */
+  DA_ELAUNCH = 4       /* the HIP runtime rejected a launch */
+} da_status;
+
+typedef enum { DA_BF16 = 0, DA_FP8_E4M3 = 1 } da_dtype;
+typedef enum { DA_MONOLITHIC = 0, DA_SPLIT = 1 } da_schedule;
+
+#define DA_BLOCK_KEYS 64  /* keys per online-softmax update */
+#define DA_CHUNK_KEYS 512 /* keys per chunk partial */
+#define DA_PAGE_SIZE 16   /* tokens per KV-cache page */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* attn_status_str(int status);
+
+/* Number of 512-key chunks for a key length: ceil(max_seqlen_k / 512), 0 for <= 0. */
+int32_t attn_num_chunks(int32_t max_seqlen_k);
+
+/* Bytes of the fp32 chunk-partial workspace for `rows` query rows:
+ *   acc [max_chunks][rows][num_heads_q][head_dim] followed by
+ *   ml  [max_chunks][rows][num_heads_q][2]   (m in log2 units, l).
+ * Returns 0 for negative arguments and SIZE_MAX on overflow. */
+size_t attn_partials_bytes(int64_t rows, int32_t num_heads_q, int32_t max_chunks,
+                           int32_t head_dim);
+
+/*
+ * Prefill / full-sequence forward / extend over packed variable-length
+ * sequences.
+ *   q        [total_q, Hq, D]   bf16 or E4M3FN codes
+ *   k, v     [total_k, Hkv, D]  bf16 or E4M3FN codes
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [batch + 1] exclusive prefix sums;
+ *            sequence b owns rows [cu_q[b], cu_q[b+1]) and keys [cu_k[b], cu_k[b+1]).
+ *   max_seqlen_q, max_seqlen_k  host upper bounds of the per-sequence lengths.
+ *   total_q, total_k            rows of q/o and of k/v; every access is clamped to them.
+ *   head_dim  64, 128 or 192.
+ *   schedule  DA_MONOLITHIC: writes o [total_q, Hq, D] bf16 and lse [total_q, Hq]
+ *                            (lse may be NULL); partials are ignored.
+ *             DA_SPLIT: writes the chunk partials of every row into `partials`
+ *                       (layout of attn_partials_bytes with rows = total_q and
+ *                       max_chunks = attn_num_chunks(max_seqlen_k)); o and lse are
+ *                       not touched.  attn_chunk_merge then produces O.
+ * Pointers q, k, v, o, partials must be 16-byte aligned; total_q must equal
+ * cu_seqlens_q[batch] for the split schedule's merge to cover only written rows.
+ */
+da_status attn_prefill_fwd(int32_t dtype, const void* q, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           int64_t total_q, int64_t total_k, int32_t num_heads_q,
+                           int32_t num_heads_kv, int32_t head_dim, float softmax_scale,
+                           int32_t causal, float q_descale, float k_descale, float v_descale,
+                           int32_t schedule, void* o, float* lse, float* partials,
+                           size_t partials_bytes, void* stream);
+
+/*
+ * Single-token decode over a paged KV cache: sequence b's query (row b of q) is
+ * the last token of a sequence of context_lens[b] tokens, so every cached key
+ * j < context_lens[b] is visible.  Token j of sequence b lives in page
+ * page_table[b * max_pages_per_seq + j / 16] at slot j % 16.
+ *   q         [batch, Hq, D]
+ *   k_cache, v_cache  element (page, slot, kv_head, d) at
+ *             page * page_stride + slot * token_stride + kv_head * head_stride + d
+ *             (element strides; e.g. [num_pages, 16, Hkv, D] has 16*Hkv*D, Hkv*D, D).
+ *   num_pages pages in each cache; table entries outside [0, num_pages) read as zero keys.
+ *   page_table device int32 [batch, max_pages_per_seq]; context_lens device int32 [batch],
+ *             each clamped to [0, max_pages_per_seq * 16].
+ *   max_context_len  host upper bound of context_lens (sizes the chunk grid).
+ *   page_size must be 16; Hq / Hkv must be at most 32.
+ *   schedule  DA_SPLIT: one workgroup per (sequence, kv head, chunk) writes the
+ *             partials (rows = batch, max_chunks = attn_num_chunks(max_context_len));
+ *             follow with attn_chunk_merge on the same stream.
+ *             DA_MONOLITHIC: one workgroup per (sequence, kv head) writes o [batch, Hq, D]
+ *             and lse directly; bit-identical to split + merge.
+ * Caches, q, o and partials must be 16-byte aligned and the byte strides
+ * multiples of 16.  Keys past a sequence's context are never read, so dead
+ * slots may hold anything (NaN included).
+ */
+da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cache,
+                                const void* v_cache, int64_t num_pages, int64_t page_stride,
+                                int64_t token_stride, int64_t head_stride,
+                                const int32_t* page_table, int32_t max_pages_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len,
+                                int32_t batch, int32_t page_size, int32_t num_heads_q,
+                                int32_t num_heads_kv, int32_t head_dim, float softmax_scale,
+                                float q_descale, float k_descale, float v_descale,
+                                int32_t schedule, float* partials, size_t partials_bytes,
+                                void* o, float* lse, void* stream);
+
+/*
+ * Fold chunk partials into O: for every (row, head), partials c = 0 .. max_chunks-1
+ * are merged left to right with the exact max/sum rescale (empty partials,
+ * m = -inf, are skipped), then O = A / L (0 when L = 0) times v_descale is
+ * rounded once to bf16.  o [rows, Hq, D] bf16, lse [rows, Hq] fp32 or NULL.
+ * v_descale is 1.0f for bf16 inputs and the V scale for E4M3FN inputs.
+ */
+da_status attn_chunk_merge(const float* partials, size_t partials_bytes, int64_t rows,
+                           int32_t num_heads_q, int32_t max_chunks, int32_t head_dim,
+                           float v_descale, void* o, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DETATTN_H */

@@ -1,0 +1,113 @@
+"""Helpers for the GPU tests: move seeded inputs to the device, run the HIP path
+through the C ABI, evaluate the oracle on the same stored values, compare."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+BF16_MAX_ABS, BF16_MEAN_ABS = 1e-2, 1e-3  # tolerances for bf16 inputs
+FP8_MAX_ABS = 6e-2                         # fp8 inputs, against the dequantised oracle
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev(t: torch.Tensor) -> torch.Tensor:
+    return t.contiguous().to("cuda")
+
+
+def oracle_inputs_prefill(inp: synth.PrefillInputs):
+    if inp.dtype == "fp8":
+        q = oracle.dequantize_e4m3(inp.q.numpy(), inp.q_scale)
+        k = oracle.dequantize_e4m3(inp.k.numpy(), inp.k_scale)
+        v = oracle.dequantize_e4m3(inp.v.numpy(), inp.v_scale)
+    else:
+        q, k, v = synth.to_f64(inp.q), synth.to_f64(inp.k), synth.to_f64(inp.v)
+    return q, k, v
+
+
+def descales(inp) -> tuple:
+    return (inp.q_scale, inp.k_scale, inp.v_scale)
+
+
+def run_prefill(inp: synth.PrefillInputs, schedule: int, return_lse: bool = False, out=None):
+    import deterministic_flash_attention_amd as dfa
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    cq, ck = dev(inp.cu_seqlens_q), dev(inp.cu_seqlens_k)
+    res = dfa.prefill(q, k, v, cq, ck, max(inp.seqlens_q), max(inp.seqlens_k), inp.causal,
+                      softmax_scale=inp.scale, schedule=schedule, descales=descales(inp),
+                      out=out, return_lse=return_lse)
+    torch.cuda.synchronize()
+    return res
+
+
+def run_decode(inp: synth.DecodeInputs, schedule: int, return_lse: bool = False, max_ctx=None):
+    import deterministic_flash_attention_amd as dfa
+    mc = int(inp.context_lens.max()) if max_ctx is None else max_ctx
+    res = dfa.decode(dev(inp.q), dev(inp.k_cache), dev(inp.v_cache), dev(inp.page_table),
+                     dev(inp.context_lens), mc, softmax_scale=inp.scale, schedule=schedule,
+                     descales=descales(inp), return_lse=return_lse)
+    torch.cuda.synchronize()
+    return res
+
+
+def compare(gpu_o: torch.Tensor, ref: np.ndarray, fp8: bool, rows=None, label: str = ""):
+    """Element-wise comparison against the oracle at the stated tolerance.
+
+    Returns (max_abs, mean_abs).  On failure reports the worst element, its
+    reference value and the bf16 spacing there."""
+    g = gpu_o.float().cpu().double().numpy()
+    if rows is not None:
+        g, ref = g[rows], ref[rows]
+    assert np.isfinite(g).all(), f"{label}: non-finite GPU output"
+    err = np.abs(g - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    idx = np.unravel_index(int(err.argmax()), err.shape)
+    ref_v = float(ref[idx])
+    ulp = 2.0 ** (math.floor(math.log2(abs(ref_v))) - 7) if ref_v != 0 else 0.0
+    note(f"{label}: max_abs={mx:.3e} mean_abs={mean:.3e} worst at {idx} ref={ref_v:.5f} "
+         f"gpu={g[idx]:.5f} bf16_ulp={ulp:.2e}")
+    if fp8:
+        assert mx <= FP8_MAX_ABS, f"{label}: fp8 max_abs {mx} > {FP8_MAX_ABS}"
+    else:
+        assert mx <= BF16_MAX_ABS, f"{label}: max_abs {mx} > {BF16_MAX_ABS}"
+        assert mean <= BF16_MEAN_ABS, f"{label}: mean_abs {mean} > {BF16_MEAN_ABS}"
+    return mx, mean
+
+
+def bits(t: torch.Tensor) -> torch.Tensor:
+    """Raw bit pattern of a bf16/fp32 tensor (for bitwise comparisons)."""
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16)
+    if t.dtype == torch.float32:
+        return t.view(torch.int32)
+    return t
+
+
+def assert_bitwise(a: torch.Tensor, b: torch.Tensor, label: str) -> None:
+    ba, bb = bits(a), bits(b)
+    same = torch.equal(ba, bb)
+    if not same:
+        diff = (ba != bb).nonzero()
+        note(f"{label}: {diff.shape[0]} differing elements, first at {diff[0].tolist()}")
+    assert same, f"{label}: not bitwise identical"
+
+
+def sample_rows(seqlens, per_seq: int, seed: int) -> np.ndarray:
+    """Global row indices: per sequence the first, last and random rows."""
+    rng = np.random.default_rng(seed)
+    rows, start = [], 0
+    for n in seqlens:
+        if n > 0:
+            pick = {0, n - 1} | set(rng.integers(0, n, size=min(per_seq, n)).tolist())
+            rows.extend(start + r for r in sorted(pick))
+        start += n
+    return np.array(rows, dtype=np.int64)

@@ -1,0 +1,136 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every entry point
+that include/detattn.h declares, and rejects malformed arguments on the host
+with the documented status before any HIP call (so these run without a GPU:
+no call here reaches a launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "detattn.h")
+
+DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EWORKSPACE, DA_ELAUNCH = range(5)
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import deterministic_flash_attention_amd as dfa
+    if not os.path.exists(dfa.library_path()):
+        from deterministic_flash_attention_amd import build
+        build.build()
+    return dfa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    assert names == sorted(["attn_status_str", "attn_num_chunks", "attn_partials_bytes",
+                            "attn_prefill_fwd", "attn_decode_split_fwd", "attn_chunk_merge"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import deterministic_flash_attention_amd as dfa
+    out = subprocess.run(["nm", "-D", "--defined-only", dfa.library_path()], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\sT\s(attn_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_small_helpers(lib):
+    assert lib.attn_num_chunks(0) == 0 and lib.attn_num_chunks(1) == 1
+    assert lib.attn_num_chunks(512) == 1 and lib.attn_num_chunks(513) == 2
+    assert lib.attn_num_chunks(32768) == 64
+    assert lib.attn_partials_bytes(8192, 32, 16, 128) == 8192 * 32 * 16 * 130 * 4
+    assert lib.attn_partials_bytes(-1, 32, 16, 128) == 0
+    for s in range(5):
+        assert lib.attn_status_str(s).decode().startswith("DA_")
+
+
+def _prefill_args(**over):
+    a = dict(dtype=0, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, batch=1, max_q=300,
+             max_k=300, total_q=300, total_k=300, hq=2, hkv=1, d=64, scale=0.125, causal=1,
+             qd=1.0, kd=1.0, vd=1.0, schedule=0, o=FAKE, lse=None, part=None, part_bytes=0,
+             stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=7), DA_EINVAL),
+    (dict(schedule=5), DA_EINVAL),
+    (dict(causal=2), DA_EINVAL),
+    (dict(d=80), DA_EUNSUPPORTED),
+    (dict(hq=3, hkv=2), DA_EINVAL),
+    (dict(hkv=0), DA_EINVAL),
+    (dict(q=None), DA_EINVAL),
+    (dict(cu_k=None), DA_EINVAL),
+    (dict(o=None), DA_EINVAL),
+    (dict(q=FAKE + 8), DA_EINVAL),          # misaligned
+    (dict(scale=0.0), DA_EINVAL),
+    (dict(scale=float("nan")), DA_EINVAL),
+    (dict(qd=0.5), DA_EINVAL),              # descales must be 1 for bf16
+    (dict(dtype=1, qd=0.0), DA_EINVAL),     # fp8 descales must be finite and positive
+    (dict(batch=-1), DA_EINVAL),
+    (dict(schedule=1, part=None), DA_EINVAL),
+    (dict(schedule=1, part=FAKE, part_bytes=1024), DA_EWORKSPACE),
+    (dict(max_q=1 << 30), DA_EUNSUPPORTED),  # beyond 32-bit descriptor offsets
+])
+def test_prefill_validation(lib, over, status):
+    assert lib.attn_prefill_fwd(*_prefill_args(**over)) == status
+
+
+def _decode_args(**over):
+    a = dict(dtype=0, q=FAKE, kc=FAKE, vc=FAKE, num_pages=100, page_stride=16 * 8 * 128,
+             token_stride=8 * 128, head_stride=128, table=FAKE, max_pages=64, ctx=FAKE,
+             max_ctx=1024, batch=4, page_size=16, hq=32, hkv=8, d=128, scale=0.088, qd=1.0,
+             kd=1.0, vd=1.0, schedule=1, part=FAKE, part_bytes=1 << 40, o=None, lse=None,
+             stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(page_size=32), DA_EUNSUPPORTED),
+    (dict(hq=64, hkv=1), DA_EUNSUPPORTED),   # more than 32 query heads per kv head
+    (dict(max_ctx=64 * 16 + 1), DA_EINVAL),  # context beyond the page table
+    (dict(num_pages=0), DA_EINVAL),
+    (dict(token_stride=0), DA_EINVAL),
+    (dict(head_stride=100), DA_EINVAL),      # 200-byte stride is not a multiple of 16
+    (dict(table=None), DA_EINVAL),
+    (dict(part=None), DA_EINVAL),
+    (dict(part_bytes=4096), DA_EWORKSPACE),
+    (dict(schedule=0, o=None), DA_EINVAL),
+    (dict(d=96), DA_EUNSUPPORTED),
+    (dict(vd=2.0), DA_EINVAL),
+])
+def test_decode_validation(lib, over, status):
+    assert lib.attn_decode_split_fwd(*_decode_args(**over)) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 1 << 40, -1, 32, 4, 128, 1.0, FAKE, None, None), DA_EINVAL),
+    ((FAKE, 1 << 40, 64, 0, 4, 128, 1.0, FAKE, None, None), DA_EINVAL),
+    ((FAKE, 1 << 40, 64, 32, 4, 100, 1.0, FAKE, None, None), DA_EUNSUPPORTED),
+    ((FAKE, 1 << 40, 64, 32, 4, 128, 0.0, FAKE, None, None), DA_EINVAL),
+    ((FAKE, 1 << 40, 64, 32, 4, 128, 1.0, None, None, None), DA_EINVAL),
+    ((FAKE, 100, 64, 32, 4, 128, 1.0, FAKE, None, None), DA_EWORKSPACE),
+    ((None, 1 << 40, 64, 32, 4, 128, 1.0, FAKE, None, None), DA_EINVAL),
+])
+def test_merge_validation(lib, args, status):
+    assert lib.attn_chunk_merge(*args) == status
+
+
+def test_zero_work_calls_return_ok_without_launch(lib):
+    # batch 0 and zero rows are no-ops that succeed before any HIP call
+    assert lib.attn_prefill_fwd(*_prefill_args(batch=0)) == DA_OK
+    assert lib.attn_chunk_merge(None, 0, 0, 32, 0, 128, 1.0, None, None, None) == DA_OK

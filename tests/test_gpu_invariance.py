@@ -1,0 +1,203 @@
+"""Bitwise invariance of the HIP path across schedules and batch composition
+(RL-Kernel page, section 2: the monolithic and split schedules are
+bit-identical, which is what makes decode agree with training; its test file
+covers prefill-vs-decode identity, batch composition and the unmasked fast
+path).  Also the store bounds: sentinel pre-fill outside the valid cells and
+the padded-row alias set (FlyDSL conv3d page, "Root cause"; aiter MQA-logits
+page, "Correctness")."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from alias_sets import packed_alias_rows
+from gpu_utils import assert_bitwise, dev, note, run_decode, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+MONO, SPLIT = 0, 1
+
+
+def _prefill(inp, schedule, **kw):
+    return run_prefill(inp, schedule, **kw)
+
+
+@pytest.mark.parametrize("case", [
+    ([300], None, 2, 1, 64, True, "bf16"),
+    ([600, 250, 1, 397], None, 8, 2, 128, True, "bf16"),
+    ([1100], None, 4, 4, 128, False, "bf16"),
+    ([100, 1, 37], [700, 513, 64], 4, 2, 128, True, "bf16"),
+    ([700], None, 4, 4, 192, True, "fp8"),
+    ([700], None, 4, 4, 192, False, "fp8"),
+])
+def test_split_equals_monolithic_prefill(case):
+    sq, sk, hq, hkv, d, causal, dt = case
+    inp = synth.prefill_inputs(31, sq, hq, hkv, d, causal, seqlens_k=sk, dtype=dt)
+    note(f"split vs mono {case}")
+    o1, l1 = _prefill(inp, MONO, return_lse=True)
+    o2, l2 = _prefill(inp, SPLIT, return_lse=True)
+    assert_bitwise(o1, o2, "O split vs monolithic")
+    assert_bitwise(l1, l2, "lse split vs monolithic")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_split_equals_monolithic_decode(dtype):
+    ctx = [1, 17, 64, 65, 512, 513, 1200, 3000]
+    inp = synth.decode_inputs(33, len(ctx), 16, 4, 128, context_lens=ctx, spare_pages=8, dtype=dtype)
+    o1, l1 = run_decode(inp, MONO, return_lse=True)
+    o2, l2 = run_decode(inp, SPLIT, return_lse=True)
+    assert_bitwise(o1, o2, "decode O split vs monolithic")
+    assert_bitwise(l1, l2, "decode lse split vs monolithic")
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp8", 192)])
+def test_decode_equals_last_prefill_row(dtype, d):
+    """The decode token of a sequence of length L equals row L-1 of its causal
+    prefill, bit for bit, for lengths around block and chunk boundaries."""
+    lens = [1, 2, 63, 64, 65, 511, 512, 513, 1000, 1537]
+    hq, hkv = 8, 2
+    inp = synth.prefill_inputs(35, lens, hq, hkv, d, True, dtype=dtype)
+    o_pre = _prefill(inp, MONO)
+    # Page the same K/V into a shuffled paged cache; the decode query is the last row.
+    ps = 16
+    pages = [(n + ps - 1) // ps for n in lens]
+    npages = sum(pages) + 5
+    perm = torch.randperm(npages, generator=torch.Generator().manual_seed(3))
+    kc = torch.zeros(npages, ps, hkv, d, dtype=inp.k.dtype)
+    vc = torch.zeros_like(kc)
+    table = torch.zeros(len(lens), max(pages), dtype=torch.int32)
+    cu = inp.cu_seqlens_k.tolist()
+    pos = 0
+    for b, n in enumerate(lens):
+        for j in range(pages[b]):
+            table[b, j] = int(perm[pos])
+            pos += 1
+        for t in range(n):
+            kc[table[b, t // ps], t % ps] = inp.k[cu[b] + t]
+            vc[table[b, t // ps], t % ps] = inp.v[cu[b] + t]
+    last = torch.tensor([cu[b + 1] - 1 for b in range(len(lens))])
+    qd = inp.q[last].contiguous()
+    dec = synth.DecodeInputs(qd, kc, vc, table, torch.tensor(lens, dtype=torch.int32), hq, hkv, d,
+                             ps, inp.scale, 0, dtype, inp.q_scale, inp.k_scale, inp.v_scale)
+    for sched in (SPLIT, MONO):
+        o_dec = run_decode(dec, sched)
+        assert_bitwise(o_dec, o_pre[last.to(o_pre.device)], f"decode({sched}) vs last prefill row")
+
+
+def test_batch_composition_and_order():
+    """A sequence's rows do not depend on the other sequences in the batch."""
+    lens = [600, 250, 1, 397, 130]
+    hq, hkv, d = 8, 2, 128
+    inp = synth.prefill_inputs(37, lens, hq, hkv, d, True)
+    o_all = _prefill(inp, MONO).cpu()
+    cu = inp.cu_seqlens_q.tolist()
+    for b, n in enumerate(lens):
+        sub = synth.PrefillInputs(inp.q[cu[b]:cu[b + 1]], inp.k[cu[b]:cu[b + 1]],
+                                  inp.v[cu[b]:cu[b + 1]], synth.cu_seqlens([n]),
+                                  synth.cu_seqlens([n]), [n], [n], hq, hkv, d, inp.scale, True)
+        o_one = _prefill(sub, MONO).cpu()
+        assert_bitwise(o_one, o_all[cu[b]:cu[b + 1]], f"sequence {b} alone vs in batch")
+    # reversed batch order
+    order = list(reversed(range(len(lens))))
+    rq = torch.cat([inp.q[cu[b]:cu[b + 1]] for b in order])
+    rk = torch.cat([inp.k[cu[b]:cu[b + 1]] for b in order])
+    rv = torch.cat([inp.v[cu[b]:cu[b + 1]] for b in order])
+    rl = [lens[b] for b in order]
+    rev = synth.PrefillInputs(rq, rk, rv, synth.cu_seqlens(rl), synth.cu_seqlens(rl), rl, rl, hq,
+                              hkv, d, inp.scale, True)
+    o_rev = _prefill(rev, SPLIT).cpu()
+    rcu = synth.cu_seqlens(rl).tolist()
+    for i, b in enumerate(order):
+        assert_bitwise(o_rev[rcu[i]:rcu[i + 1]], o_all[cu[b]:cu[b + 1]], f"seq {b} reordered")
+
+
+def test_decode_batch_composition():
+    ctx = [5, 900, 64, 2100]
+    inp = synth.decode_inputs(39, len(ctx), 8, 2, 128, context_lens=ctx, spare_pages=4)
+    o_all = run_decode(inp, SPLIT).cpu()
+    for b in range(len(ctx)):
+        one = synth.DecodeInputs(inp.q[b:b + 1], inp.k_cache, inp.v_cache, inp.page_table[b:b + 1],
+                                 inp.context_lens[b:b + 1], 8, 2, 128, 16, inp.scale)
+        assert_bitwise(run_decode(one, SPLIT).cpu(), o_all[b:b + 1], f"decode seq {b} alone")
+
+
+def test_unmasked_fast_path_equals_masked_path():
+    """The last row of a causal sequence sees every key, as does every row of
+    the dense run; in the causal run the last tile's diagonal blocks take the
+    masked path, in the dense run all blocks take the fast path."""
+    for n in (1024, 1000, 777):
+        inp_c = synth.prefill_inputs(41, [n], 4, 2, 128, True)
+        inp_d = synth.prefill_inputs(41, [n], 4, 2, 128, False)
+        oc = _prefill(inp_c, MONO)
+        od = _prefill(inp_d, MONO)
+        assert_bitwise(oc[n - 1], od[n - 1], f"last row causal vs dense n={n}")
+
+
+def test_repeat_runs_bitwise():
+    inp = synth.prefill_inputs(43, [600, 250, 1, 397], 8, 2, 128, True)
+    ref = _prefill(inp, MONO)
+    for _ in range(4):
+        assert_bitwise(_prefill(inp, MONO), ref, "repeat monolithic")
+        assert_bitwise(_prefill(inp, SPLIT), ref, "repeat split")
+
+
+def test_closed_form_rows_bitwise():
+    """Causal row 0 and a length-1 sequence see one key: O = V[that key] exactly."""
+    lens = [300, 1, 129]
+    inp = synth.prefill_inputs(45, lens, 4, 2, 64, True)
+    o = _prefill(inp, MONO).cpu()
+    cu = inp.cu_seqlens_q.tolist()
+    for b in range(3):
+        for h in range(4):
+            assert_bitwise(o[cu[b], h], inp.v[cu[b], h // 2], f"row 0 of seq {b} head {h}")
+    dec = synth.decode_inputs(47, 3, 4, 1, 128, context_lens=[1, 1, 1], spare_pages=2)
+    od = run_decode(dec, SPLIT).cpu()
+    for b in range(3):
+        page = int(dec.page_table[b, 0])
+        for h in range(4):
+            assert_bitwise(od[b, h], dec.v_cache[page, 0, 0], f"decode ctx=1 seq {b}")
+
+
+def test_sentinel_survives_outside_valid_rows():
+    """O pre-filled with NaN plus guard rows before and after; only the rows of
+    the sequences are written, the guards and an unowned tail keep the NaN."""
+    lens = [300, 1, 129]
+    hq, hkv, d = 4, 2, 64
+    inp = synth.prefill_inputs(49, lens, hq, hkv, d, True)
+    total = sum(lens)
+    guard = 200
+    for sched in (MONO, SPLIT):
+        extra = 50 if sched == MONO else 0  # unowned rows only for the monolithic schedule
+        buf = torch.full((total + 2 * guard + extra, hq, d), float("nan"), dtype=torch.bfloat16,
+                         device="cuda")
+        q = torch.cat([inp.q, torch.zeros(extra, hq, d, dtype=inp.q.dtype)])
+        pinp = synth.PrefillInputs(q, inp.k, inp.v, inp.cu_seqlens_q, inp.cu_seqlens_k, lens, lens,
+                                   hq, hkv, d, inp.scale, True)
+        out = buf[guard:guard + total + extra]
+        run_prefill(pinp, sched, out=out)
+        assert not torch.isnan(out[:total].float()).any()
+        assert torch.isnan(out[total:].float()).all(), "unowned rows were written"
+        assert torch.isnan(buf[:guard].float()).all(), "guard before O was written"
+        assert torch.isnan(buf[guard + total + extra:].float()).all(), "guard after O was written"
+
+
+def test_padded_rows_do_not_alias_next_sequence():
+    """Each sequence is run alone (batch of one, via an offset cu_seqlens view)
+    into the shared packed O after its successors were written; the rows that
+    an unguarded store of its tail tile would hit (predicted set) must keep the
+    successors' values."""
+    lens = [4096, 2500, 1, 3969]
+    hq, hkv, d = 2, 1, 128
+    import deterministic_flash_attention_amd as dfa
+    inp = synth.prefill_inputs(51, lens, hq, hkv, d, True)
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    cq, ck = dev(inp.cu_seqlens_q), dev(inp.cu_seqlens_k)
+    ref = dfa.prefill(q, k, v, cq, ck, max(lens), max(lens), True)
+    out = torch.full_like(ref, float("nan"))
+    for b in reversed(range(len(lens))):
+        dfa.attn_prefill_fwd(q, k, v, cq[b:b + 2], ck[b:b + 2], lens[b], lens[b],
+                             1.0 / np.sqrt(d), True, dfa.MONOLITHIC, o=out)
+    torch.cuda.synchronize()
+    assert_bitwise(out, ref, "sequences written one by one, last to first")
+    alias = packed_alias_rows(lens, 128)
+    assert sum(len(r) for r, _ in alias) == 60 + 127  # the predicted clobber set is non-empty

@@ -1,0 +1,170 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element, at the stated tolerances
+(bf16: max_abs <= 1e-2 and mean_abs <= 1e-3; fp8: max_abs <= 6e-2 against the
+oracle on the dequantised inputs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_utils import (compare, note, oracle_inputs_prefill, run_decode, run_prefill,
+                       sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+MONO, SPLIT = 0, 1
+
+
+def _prefill_case(seqlens_q, seqlens_k, hq, hkv, d, causal, dtype, seed, schedule, rows=None):
+    inp = synth.prefill_inputs(seed, seqlens_q, hq, hkv, d, causal, seqlens_k=seqlens_k,
+                               dtype=dtype)
+    note(f"prefill {dtype} q={seqlens_q} k={seqlens_k} hq={hq} hkv={hkv} d={d} causal={causal} "
+         f"seed={seed} schedule={schedule}")
+    o, lse = run_prefill(inp, schedule, return_lse=True)
+    q, k, v = oracle_inputs_prefill(inp)
+    ref, ref_lse = oracle.attention(q, k, v, inp.cu_seqlens_q.numpy(), inp.cu_seqlens_k.numpy(),
+                                    hq, hkv, inp.scale, causal, rows=rows)
+    compare(o, ref, dtype == "fp8", rows=rows, label="O")
+    lg = lse.cpu().double().numpy()
+    lr = ref_lse if rows is None else ref_lse[rows]
+    lg = lg if rows is None else lg[rows]
+    assert np.array_equal(np.isneginf(lg), np.isneginf(lr))
+    fin = np.isfinite(lr)
+    if fin.any():
+        assert np.abs(lg[fin] - lr[fin]).max() < 2e-3
+    return inp, o
+
+
+@pytest.mark.parametrize("schedule", [MONO, SPLIT])
+def test_tiny_causal_gqa(schedule):
+    # 300 rows: not a multiple of 64 or 128, three 128-row tiles with 84 padded rows
+    for seed in range(3):
+        _prefill_case([300], None, 2, 1, 64, True, "bf16", seed, schedule)
+
+
+@pytest.mark.parametrize("schedule", [MONO, SPLIT])
+def test_dense_ragged_multi_chunk(schedule):
+    _prefill_case([1100], None, 4, 4, 128, False, "bf16", 7, schedule)
+
+
+@pytest.mark.parametrize("schedule", [MONO, SPLIT])
+def test_causal_gqa_varlen_small(schedule):
+    _prefill_case([600, 250, 1, 397], None, 8, 2, 128, True, "bf16", 3, schedule)
+
+
+@pytest.mark.parametrize("schedule", [MONO, SPLIT])
+def test_extend_bottom_right(schedule):
+    # prefix-cached extend: fewer queries than keys, causal aligned bottom-right
+    _prefill_case([100, 1, 37], [700, 513, 64], 4, 2, 128, True, "bf16", 5, schedule)
+
+
+def test_more_queries_than_keys_all_masked_rows():
+    inp, o = _prefill_case([200], [70], 2, 1, 64, True, "bf16", 9, MONO)
+    assert torch.all(o[:130].float() == 0)
+
+
+def test_empty_and_zero_key_sequences():
+    _prefill_case([0, 130, 5], [0, 130, 0], 2, 2, 64, False, "bf16", 11, MONO)
+    _prefill_case([0, 130, 5], [0, 130, 0], 2, 2, 64, False, "bf16", 11, SPLIT)
+
+
+def test_head_dim_192_bf16():
+    _prefill_case([333], None, 2, 1, 192, True, "bf16", 13, MONO)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("schedule", [MONO, SPLIT])
+def test_fp8_wide_head_small(causal, schedule):
+    _prefill_case([700], None, 4, 4, 192, causal, "fp8", 17, schedule)
+
+
+def test_fp8_head_dim_128():
+    _prefill_case([300, 129], None, 4, 2, 128, True, "fp8", 19, MONO)
+
+
+# ---------------------------------------------------------------- decode
+def _decode_case(ctx, hq, hkv, d, seed, schedule, dtype="bf16", spare=16):
+    inp = synth.decode_inputs(seed, len(ctx), hq, hkv, d, context_lens=ctx, spare_pages=spare,
+                              dtype=dtype)
+    note(f"decode {dtype} ctx={ctx[:8]}.. hq={hq} hkv={hkv} d={d} seed={seed} sched={schedule}")
+    o, lse = run_decode(inp, schedule, return_lse=True)
+    if dtype == "fp8":
+        q = oracle.dequantize_e4m3(inp.q.numpy(), inp.q_scale)
+        kc = oracle.dequantize_e4m3(inp.k_cache.numpy(), inp.k_scale)
+        vc = oracle.dequantize_e4m3(inp.v_cache.numpy(), inp.v_scale)
+    else:
+        q, kc, vc = synth.to_f64(inp.q), inp.k_cache.float().numpy(), inp.v_cache.float().numpy()
+    ref, ref_lse = oracle.paged_decode(q, kc, vc, inp.page_table.numpy(), inp.context_lens.numpy(),
+                                       hq, hkv, inp.scale, inp.page_size)
+    compare(o, ref, dtype == "fp8", label="decode O")
+    lg = lse.cpu().double().numpy()
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isneginf(lg), np.isneginf(ref_lse))
+    if fin.any():
+        assert np.abs(lg[fin] - ref_lse[fin]).max() < 2e-3
+    return inp, o
+
+
+CTX_SMALL = [1, 15, 16, 17, 63, 64, 65, 511, 512, 513, 1500, 2047]
+
+
+@pytest.mark.parametrize("schedule", [SPLIT, MONO])
+def test_decode_small(schedule):
+    _decode_case(CTX_SMALL, 32, 8, 128, 21, schedule)
+
+
+def test_decode_gqa_group_2_head_dim_64():
+    _decode_case([5, 700, 1025], 4, 2, 64, 23, SPLIT)
+
+
+def test_decode_fp8():
+    _decode_case([3, 600, 1700], 8, 2, 128, 25, SPLIT, dtype="fp8")
+
+
+def test_decode_zero_context():
+    inp, o = _decode_case([0, 40], 4, 1, 128, 27, SPLIT)
+    assert torch.all(o[0].float() == 0)
+
+
+# ------------------------------------------- full-size workloads, sampled rows
+def test_full_dense_prefill_sampled():
+    cfg = synth.DENSE_PREFILL
+    rows = sample_rows(cfg["seqlens"], 48, 1)
+    _prefill_case(cfg["seqlens"], None, cfg["hq"], cfg["hkv"], cfg["d"], False, "bf16", 0, MONO,
+                  rows=rows)
+
+
+def test_full_causal_varlen_sampled():
+    cfg = synth.CAUSAL_VARLEN
+    rows = sample_rows(cfg["seqlens"], 24, 2)
+    _prefill_case(cfg["seqlens"], None, cfg["hq"], cfg["hkv"], cfg["d"], True, "bf16", 0, MONO,
+                  rows=rows)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_fp8_wide_head_sampled(causal):
+    cfg = synth.FP8_WIDE
+    rows = sample_rows(cfg["seqlens"], 32, 3)
+    _prefill_case(cfg["seqlens"], None, cfg["hq"], cfg["hkv"], cfg["d"], causal, "fp8", 0, MONO,
+                  rows=rows)
+
+
+def test_full_paged_decode_sampled_sequences():
+    cfg = synth.PAGED_DECODE
+    inp = synth.decode_inputs(0, cfg["batch"], cfg["hq"], cfg["hkv"], cfg["d"],
+                              ctx_min=cfg["ctx_min"], ctx_max=cfg["ctx_max"],
+                              spare_pages=cfg["spare_pages"])
+    note(f"full decode: sum ctx = {int(inp.context_lens.sum())}")
+    o = run_decode(inp, SPLIT)
+    pick = np.random.default_rng(4).choice(cfg["batch"], size=12, replace=False)
+    pt, ctx = inp.page_table.numpy(), inp.context_lens.numpy()
+    q = synth.to_f64(inp.q)
+    for b in pick:
+        j = torch.arange(int(ctx[b]))
+        pages = torch.from_numpy(pt[b]).long()[j // 16]
+        kb = inp.k_cache[pages, j % 16].double().numpy()
+        vb = inp.v_cache[pages, j % 16].double().numpy()
+        ref, _ = oracle.attention(q[b:b + 1], kb, vb, [0, 1], [0, int(ctx[b])], cfg["hq"],
+                                  cfg["hkv"], inp.scale, True)
+        compare(o[b:b + 1], ref, False, label=f"decode seq {b} ctx {ctx[b]}")
