@@ -18,12 +18,15 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdetattn.so")
 SOURCES = ["abi.cpp", "prefill.hip", "decode.hip", "merge.hip"]
 
-# -ffp-contract=off: no fused multiply-add anywhere (part of the numerical contract).
+# -ffp-contract=off: the compiler fuses no multiply-add (part of the numerical contract).
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-fno-fast-math", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # MFMA accumulators in VGPRs: the softmax rescales them every block, and an
+    # AGPR-resident accumulator costs a read and a write move per element there.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -77,8 +77,10 @@ __device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cas
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
 }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two floats to a packed bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)bf16_bits(lo) | ((uint32_t)bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 // Four OCP E4M3FN codes (one dword) to four bf16 values; exact, since every
 // E4M3FN value is representable in bf16.

@@ -14,11 +14,11 @@
 //     inputs), D/16 K-steps in ascending order from a zero accumulator; the
 //     instruction shape and the K order are part of the contract, as the same
 //     page says of its GEMM sibling (section 1);
-//   * scores are multiplied once by c = scale * q_descale * k_descale * log2(e)
-//     and masked by select, never by adding;
-//   * row max over the block (exact in any order), then
-//     alpha = exp2(m - m'), p = exp2(s - m') with v_exp_f32, a fixed row-sum
-//     tree, l = l*alpha + sum(p); a row whose block is fully masked keeps
+//   * scores are masked by select (to -inf), never by adding; the block max is
+//     m_blk = c * max(raw scores) with c = scale * q_descale * k_descale * log2(e),
+//     m' = max(m, m_blk), alpha = exp2(m - m'), p = exp2(fma(s, c, -m')) with
+//     v_exp_f32 and one explicit fused multiply-add, a fixed row-sum tree,
+//     l = l*alpha + sum(p); a row whose block is fully masked keeps
 //     m, l and acc bit for bit (alpha = 1, p = 0, and its empty state uses the
 //     safe max 0 so no -inf - -inf appears);
 //   * P is rounded to bf16 (nearest even) and acc = (acc*alpha) + P V on
@@ -30,7 +30,8 @@
 //     b = exp2(m_c - M'), L = L*a + l_c*b, A = A*a + acc_c*b);
 //   * O = L > 0 ? A / L : 0 (IEEE division) times v_descale, rounded once to bf16.
 //
-// All code is built with -ffp-contract=off: no multiply-add is fused, so each
+// All code is built with -ffp-contract=off: the compiler fuses no multiply-add,
+// so apart from the one explicit fused multiply-add in the exponent, each
 // product and sum above is a separately rounded fp32 operation in every kernel.
 #pragma once
 
@@ -48,9 +49,15 @@ struct Geom {
   static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim must be a multiple of 32");
   static constexpr int kEs = FP8 ? 1 : 2;       // bytes per Q/K/V element in HBM
   static constexpr int kRowBytes = D * kEs;     // one head row of Q/K/V
-  static constexpr int kQRow = kRowBytes + 16;  // LDS row strides (padded by 16 B)
-  static constexpr int kKRow = kRowBytes + 16;
-  static constexpr int kVRow = D * 2 + 16;      // V is staged as bf16
+  // LDS row strides, chosen for gfx950's 64 four-byte banks (256 bytes per
+  // cycle).  K rows are read 16 bytes (bf16) or 8 bytes (fp8) per lane, 16 or
+  // 32 lanes per cycle, one row per lane: an odd number of access units per
+  // row puts those rows on distinct banks.  V rows are read by the transposing
+  // read, four rows x 64 bytes per 32-lane cycle: a stride of 64 mod 256 bytes
+  // puts the four rows on disjoint banks.
+  static constexpr int kQRow = kRowBytes + 16;
+  static constexpr int kKRow = kRowBytes + (FP8 ? 8 : 16);
+  static constexpr int kVRow = D * 2 + 64;      // V is staged as bf16
   static constexpr int kKStage = kBlockKeys * kKRow;
   static constexpr int kVStage = kBlockKeys * kVRow;
   static constexpr int kSteps = D / 16;         // QK^T K-steps
@@ -99,6 +106,34 @@ __device__ __forceinline__ void qk_scores(f32x16 (&s)[2], const QFrag<FP8> (&q)[
   }
 }
 
+// Same product with the Q^T operands read from the wave's rows of the LDS Q tile
+// (qs points at the wave's first row; row stride G::kQRow) instead of registers.
+template <int D, bool FP8>
+__device__ __forceinline__ void qk_scores_qlds(f32x16 (&s)[2], const unsigned char* qs,
+                                               const unsigned char* ks, int lane) {
+  using G = Geom<D, FP8>;
+  const int row = key_sigma(lane & 31);
+  const int h = lane >> 5;
+  const unsigned char* qrow = qs + (lane & 31) * G::kQRow;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < G::kSteps; ++st) {
+    const uint32_t qoff = (uint32_t)((16 * st + 8 * h) * G::kEs);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t off = (uint32_t)((32 * t + row) * G::kKRow + (16 * st + 8 * h) * G::kEs);
+      if constexpr (FP8) {
+        s[t] = mfma_fp8(lds_load8(ks, off), lds_load8(qrow, qoff), s[t]);
+      } else {
+        s[t] = mfma_bf16(lds_load16(ks, off), lds_load16(qrow, qoff), s[t]);
+      }
+    }
+  }
+}
+
 // Online-softmax update of one lane's query column over a 64-key block.
 // rel_lim: keys at block offset >= rel_lim are masked (MASKED only).
 // Returns alpha for the accumulator and P^T as four bf16x8 PV operands.
@@ -106,27 +141,32 @@ template <bool MASKED>
 __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float c, int rel_lim,
                                               float& m, float& l, float& alpha,
                                               u32x4 (&pb)[4]) {
+  // The row max is taken on the raw dot products: fl(c * s) is monotonic in s
+  // for c > 0, so fl(c * max s) is exactly the max of the scaled scores.
   float x[2][16];
-  float mb = -INFINITY;
+  float mr = -INFINITY;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float v = s[t][i] * c;
+      float v = s[t][i];
       if constexpr (MASKED) v = (score_key(t, i, h) < rel_lim) ? v : -INFINITY;
       x[t][i] = v;
-      mb = fmaxf(mb, v);
+      mr = fmaxf(mr, v);
     }
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  mr = fmaxf(mr, __shfl_xor(mr, 32));
+  const float mb = mr * c;
   const float mn = fmaxf(m, mb);
   const bool empty = (mn == -INFINITY);
-  const float msafe = empty ? 0.0f : mn;
+  const float nms = empty ? 0.0f : -mn;
   alpha = empty ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+  // p = exp2(c * s - m'), the product and difference in one explicit fused
+  // multiply-add (one rounding); masked scores are -inf and give p = 0.
   float p[2][16];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[t][i] = __builtin_amdgcn_exp2f(x[t][i] - msafe);
+    for (int i = 0; i < 16; ++i) p[t][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[t][i], c, nms));
   // Row-sum tree: pair the two key tiles, then halve 16 -> 1, then add the
   // other half-wave (lane ^ 32), which holds the remaining 32 keys.
   float u[16];
@@ -154,7 +194,7 @@ template <int D, int NT>
 __device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[NT], int dt0, float alpha,
                                               const u32x4 (&pb)[4], const unsigned char* vs,
                                               int lane) {
-  constexpr int kVRow = D * 2 + 16;
+  constexpr int kVRow = D * 2 + 64;
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -168,14 +208,9 @@ __device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[NT], int dt0, float 
     for (int j = 0; j < NT; ++j) {
       const int d = 32 * (dt0 + j) + 16 * (grp & 1) + dq;
       const uint32_t off0 = (uint32_t)((16 * kk + 8 * h + key_r) * kVRow + d * 2);
-      const s16x4 lo = lds_load_tr16(vs, off0);
-      const s16x4 hi = lds_load_tr16(vs, off0 + 4 * kVRow);
-      u32x4 a;
-      a[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-      a[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-      a[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-      a[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-      acc[j] = mfma_bf16(a, pb[kk], acc[j]);
+      const u32x2 lo = __builtin_bit_cast(u32x2, lds_load_tr16(vs, off0));
+      const u32x2 hi = __builtin_bit_cast(u32x2, lds_load_tr16(vs, off0 + 4 * kVRow));
+      acc[j] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[kk], acc[j]);
     }
   }
 }

@@ -163,37 +163,38 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
     stg.load(p, kc, vc, table, blk_begin * kBlockKeys, ctx, head_off, tid);
     stg.store(sK, sV, tid);
     __syncthreads();
-    for (int blk = blk_begin; blk < blk_end; ++blk) {
-      const int cur = (blk - blk_begin) & 1;
-      const bool more = blk + 1 < blk_end;
-      if (more) stg.load(p, kc, vc, table, (blk + 1) * kBlockKeys, ctx, head_off, tid);
-      const unsigned char* ks = sK + cur * G::kKStage;
-      const unsigned char* vs = sV + cur * G::kVStage;
-      f32x16 s[2];
-      qk_scores<D, FP8>(s, qf, ks, lane);
-      float alpha;
-      u32x4 pb[4];
-      if (kBlockKeys * (blk + 1) <= ctx) {
-        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
-      } else {
-        softmax_block<true>(s, h, c, ctx - kBlockKeys * blk, m, l, alpha, pb);
-      }
-      pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
-      if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
-      __syncthreads();
-      if constexpr (!SPLIT) {
-        if (((blk + 1) % kBlocksPerChunk) == 0 || !more) {
-          float ca, cb;
-          int mode;
-          merge_stats(M, L, m, l, ca, cb, mode);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            A[0][i] = merge_elem(A[0][i], acc[0][i], mode, ca, cb);
-            acc[0][i] = 0.0f;
-          }
-          m = -INFINITY;
-          l = 0.0f;
+    for (int blk = blk_begin; blk < blk_end;) {
+      const int cend = min(blk_end, (blk / kBlocksPerChunk + 1) * kBlocksPerChunk);
+      for (; blk < cend; ++blk) {
+        const int cur = (blk - blk_begin) & 1;
+        const bool more = blk + 1 < blk_end;
+        if (more) stg.load(p, kc, vc, table, (blk + 1) * kBlockKeys, ctx, head_off, tid);
+        const unsigned char* ks = sK + cur * G::kKStage;
+        const unsigned char* vs = sV + cur * G::kVStage;
+        f32x16 s[2];
+        qk_scores<D, FP8>(s, qf, ks, lane);
+        float alpha;
+        u32x4 pb[4];
+        if (kBlockKeys * (blk + 1) <= ctx) {
+          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+        } else {
+          softmax_block<true>(s, h, c, ctx - kBlockKeys * blk, m, l, alpha, pb);
         }
+        pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
+        if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
+        __syncthreads();
+      }
+      if constexpr (!SPLIT) {
+        float ca, cb;
+        int mode;
+        merge_stats(M, L, m, l, ca, cb, mode);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          A[0][i] = merge_elem(A[0][i], acc[0][i], mode, ca, cb);
+          acc[0][i] = 0.0f;
+        }
+        m = -INFINITY;
+        l = 0.0f;
       }
     }
   }

@@ -195,53 +195,43 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p)
     stg.store(sK, sV, tid);
     __syncthreads();
 
-    QFrag<FP8> qf[G::kSteps];
-    {
-      const int row = 32 * wave + (lane & 31);
-#pragma unroll
-      for (int st = 0; st < G::kSteps; ++st) {
-        const uint32_t off = (uint32_t)(row * G::kQRow + (16 * st + 8 * h) * G::kEs);
-        if constexpr (FP8) {
-          qf[st].v = lds_load8(sQ, off);
-        } else {
-          qf[st].v = lds_load16(sQ, off);
-        }
-      }
-    }
+    const unsigned char* const sQw = sQ + (32 * wave) * G::kQRow;  // this wave's Q rows
 
-    for (int blk = blk_begin; blk < blk_end; ++blk) {
-      const int cur = (blk - blk_begin) & 1;
-      const bool more = blk + 1 < blk_end;
-      if (more) stg.load(kr, vr, (blk + 1) * kBlockKeys, kv_row_bytes, tid);
-      const unsigned char* ks = sK + cur * G::kKStage;
-      const unsigned char* vs = sV + cur * G::kVStage;
-      f32x16 s[2];
-      qk_scores<D, FP8>(s, qf, ks, lane);
-      float alpha;
-      u32x4 pb[4];
-      if (kBlockKeys * (blk + 1) <= kfull) {
-        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
-      } else {
-        softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
-      }
-      pv_accumulate<D, NT>(acc, 0, alpha, pb, vs, lane);
-      if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
-      __syncthreads();
-      if constexpr (!SPLIT) {
-        if (((blk + 1) % kBlocksPerChunk) == 0 || !more) {
-          float ca, cb;
-          int mode;
-          merge_stats(M, L, m, l, ca, cb, mode);
-#pragma unroll
-          for (int j = 0; j < NT; ++j)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              A[j][i] = merge_elem(A[j][i], acc[j][i], mode, ca, cb);
-              acc[j][i] = 0.0f;
-            }
-          m = -INFINITY;
-          l = 0.0f;
+    for (int blk = blk_begin; blk < blk_end;) {
+      const int cend = min(blk_end, (blk / kBlocksPerChunk + 1) * kBlocksPerChunk);
+      for (; blk < cend; ++blk) {
+        const int cur = (blk - blk_begin) & 1;
+        const bool more = blk + 1 < blk_end;
+        if (more) stg.load(kr, vr, (blk + 1) * kBlockKeys, kv_row_bytes, tid);
+        const unsigned char* ks = sK + cur * G::kKStage;
+        const unsigned char* vs = sV + cur * G::kVStage;
+        f32x16 s[2];
+        qk_scores_qlds<D, FP8>(s, sQw, ks, lane);
+        float alpha;
+        u32x4 pb[4];
+        if (kBlockKeys * (blk + 1) <= kfull) {
+          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+        } else {
+          softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
         }
+        pv_accumulate<D, NT>(acc, 0, alpha, pb, vs, lane);
+        if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
+        __syncthreads();
+      }
+      if constexpr (!SPLIT) {
+        // End of a 512-key chunk: fold its partial into the running total.
+        float ca, cb;
+        int mode;
+        merge_stats(M, L, m, l, ca, cb, mode);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            A[j][i] = merge_elem(A[j][i], acc[j][i], mode, ca, cb);
+            acc[j][i] = 0.0f;
+          }
+        m = -INFINITY;
+        l = 0.0f;
       }
     }
   }
