@@ -38,7 +38,6 @@ struct PrefillCfg {
   static constexpr int kLds = kVOff + 2 * G::kVStage;
   // Q tile, the two K stages and the two V stages are disjoint byte ranges.
   static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * G::kKStage, "LDS regions overlap");
-  static_assert(kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
 };
 
 __device__ __forceinline__ uint32_t extent_bytes(int64_t nrows, int64_t row_bytes,
@@ -96,6 +95,7 @@ template <int D, bool FP8, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p) {
   using G = Geom<D, FP8>;
   using C = PrefillCfg<D, FP8, NW>;
+  static_assert(C::kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
   constexpr int NT = G::kDTiles;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
   unsigned char* const sQ = smem;
@@ -299,25 +299,37 @@ hipError_t launch_one(const PrefillParams& p, bool split, hipStream_t stream) {
   return hipGetLastError();
 }
 
-constexpr int kPrefillWaves = 4;
+// Waves per workgroup: eight (two per SIMD, so one wave's MFMAs overlap the
+// other's softmax) up to D = 128, where a wave's registers fit in the 256
+// that two waves per SIMD leave it; four (one per SIMD) for wider heads.
+template <int D, bool FP8>
+constexpr int prefill_waves() {
+  return D <= 128 ? 8 : 4;
+}
 
 }  // namespace
 
-int prefill_tile_rows(int, bool) { return 32 * kPrefillWaves; }
+int prefill_tile_rows(int head_dim, bool fp8) {
+  switch (head_dim) {
+    case 64: return 32 * (fp8 ? prefill_waves<64, true>() : prefill_waves<64, false>());
+    case 128: return 32 * (fp8 ? prefill_waves<128, true>() : prefill_waves<128, false>());
+    case 192: return 32 * (fp8 ? prefill_waves<192, true>() : prefill_waves<192, false>());
+    default: return 32 * 8;
+  }
+}
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, bool split,
                           hipStream_t stream) {
-  constexpr int NW = kPrefillWaves;
   switch (head_dim) {
     case 64:
-      return fp8 ? launch_one<64, true, NW>(p, split, stream)
-                 : launch_one<64, false, NW>(p, split, stream);
+      return fp8 ? launch_one<64, true, prefill_waves<64, true>()>(p, split, stream)
+                 : launch_one<64, false, prefill_waves<64, false>()>(p, split, stream);
     case 128:
-      return fp8 ? launch_one<128, true, NW>(p, split, stream)
-                 : launch_one<128, false, NW>(p, split, stream);
+      return fp8 ? launch_one<128, true, prefill_waves<128, true>()>(p, split, stream)
+                 : launch_one<128, false, prefill_waves<128, false>()>(p, split, stream);
     case 192:
-      return fp8 ? launch_one<192, true, NW>(p, split, stream)
-                 : launch_one<192, false, NW>(p, split, stream);
+      return fp8 ? launch_one<192, true, prefill_waves<192, true>()>(p, split, stream)
+                 : launch_one<192, false, prefill_waves<192, false>()>(p, split, stream);
     default:
       return hipErrorInvalidValue;
   }
