@@ -106,15 +106,14 @@ __device__ __forceinline__ void qk_scores(f32x16 (&s)[2], const QFrag<FP8> (&q)[
   }
 }
 
-// Same product with the Q^T operands read from the wave's rows of the LDS Q tile
-// (qs points at the wave's first row; row stride G::kQRow) instead of registers.
+// Same product with the lane's Q^T operands read from LDS: qrow points at the
+// lane's query row (row stride irrelevant; D elements of Q).
 template <int D, bool FP8>
-__device__ __forceinline__ void qk_scores_qlds(f32x16 (&s)[2], const unsigned char* qs,
+__device__ __forceinline__ void qk_scores_qrow(f32x16 (&s)[2], const unsigned char* qrow,
                                                const unsigned char* ks, int lane) {
   using G = Geom<D, FP8>;
   const int row = key_sigma(lane & 31);
   const int h = lane >> 5;
-  const unsigned char* qrow = qs + (lane & 31) * G::kQRow;
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -132,6 +131,14 @@ __device__ __forceinline__ void qk_scores_qlds(f32x16 (&s)[2], const unsigned ch
       }
     }
   }
+}
+
+// Same product with the Q^T operands read from the wave's rows of the LDS Q tile
+// (qs points at the wave's first row; row stride G::kQRow).
+template <int D, bool FP8>
+__device__ __forceinline__ void qk_scores_qlds(f32x16 (&s)[2], const unsigned char* qs,
+                                               const unsigned char* ks, int lane) {
+  qk_scores_qrow<D, FP8>(s, qs + (lane & 31) * Geom<D, FP8>::kQRow, ks, lane);
 }
 
 // Online-softmax update of one lane's query column over a 64-key block.

@@ -22,6 +22,8 @@ namespace detattn {
 namespace {
 
 constexpr int kPageSize = 16;
+constexpr int kPagesPerBlock = kBlockKeys / kPageSize;
+constexpr int kSplitChunks = 4;  // consecutive chunks per split workgroup
 
 template <int D, bool FP8>
 struct DecodeCfg {
@@ -44,11 +46,14 @@ struct PagedStager {
   u32x4 kreg[C::kPerThread];
   u32x4 vreg[C::kPerThread];
 
-  // Keys at or past ctx, and keys whose page index is outside the cache, are
-  // staged as zeros, so dead slots (whatever they hold) never reach the MFMA.
-  __device__ __forceinline__ void load(const DecodeParams& p, const unsigned char* kc,
-                                       const unsigned char* vc, const int32_t* table, int key0,
-                                       int ctx, int64_t head_off, int tid) {
+  // Keys at or past ctx, and keys whose page is outside the cache (base < 0),
+  // are staged as zeros, so dead slots (whatever they hold) never reach the
+  // MFMA.  page_base(j) returns the element offset of token j's page for this
+  // kv head (slot 0), or -1.
+  template <typename PageBase>
+  __device__ __forceinline__ void load(const unsigned char* kc, const unsigned char* vc, int key0,
+                                       int ctx, int64_t token_stride, int tid,
+                                       const PageBase& page_base) {
 #pragma unroll
     for (int u = 0; u < C::kPerThread; ++u) {
       const int x = tid + u * C::kThreads;
@@ -56,9 +61,9 @@ struct PagedStager {
       const int j = key0 + r;
       u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
       if (j < ctx) {
-        const int64_t page = table[j / kPageSize];
-        if (page >= 0 && page < p.num_pages) {
-          const int64_t e = page * p.page_stride + (int64_t)(j % kPageSize) * p.token_stride + head_off;
+        const int64_t base = page_base(j);
+        if (base >= 0) {
+          const int64_t e = base + (int64_t)(j % kPageSize) * token_stride;
           const int64_t byte = e * G::kEs + (int64_t)col * 16;
           kv = *reinterpret_cast<const u32x4*>(kc + byte);
           vv = *reinterpret_cast<const u32x4*>(vc + byte);
@@ -92,58 +97,67 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
   using G = Geom<D, FP8>;
   using C = DecodeCfg<D, FP8>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
+  __shared__ int64_t sPage[kSplitChunks * kBlocksPerChunk * kPagesPerBlock];
+  // Q rows live in dynamic LDS sized at launch for the group: (G + 1) rows.
+  extern __shared__ __attribute__((aligned(16))) unsigned char sQ[];
   unsigned char* const sK = smem + C::kKOff;
   unsigned char* const sV = smem + C::kVOff;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
+  // Work decode: split workgroups own kSplitChunks consecutive chunks of one
+  // (sequence, kv head); monolithic workgroups own a whole (sequence, kv head).
+  // The kv head varies fastest, so the workgroups reading the same cache pages
+  // (one 256-byte row per token and head) run side by side.
   int id = blockIdx.x;
-  int chunk = 0;
-  if constexpr (SPLIT) {
-    chunk = id % p.cmax;
-    id /= p.cmax;
-  }
   const int g = id % p.hkv;
-  const int b = id / p.hkv;
+  id /= p.hkv;
+  int cgrp = 0;
+  if constexpr (SPLIT) {
+    const int ngroups = (p.cmax + kSplitChunks - 1) / kSplitChunks;
+    cgrp = id % ngroups;
+    id /= ngroups;
+  }
+  const int b = id;
   const int grp = p.group;
 
   int ctx = uniform(p.ctx_lens[b]);
   ctx = max(0, min(ctx, p.max_pages * kPageSize));
   const int nblk = (ctx + kBlockKeys - 1) / kBlockKeys;
+  const int nch = (ctx + kChunkKeys - 1) / kChunkKeys;
   int blk_begin = 0, blk_end = nblk;
-  if constexpr (SPLIT) {
-    blk_begin = chunk * kBlocksPerChunk;
-    blk_end = min(blk_begin + kBlocksPerChunk, nblk);
-  }
-
   const int64_t row_head = (int64_t)b * p.hq + (int64_t)g * grp;  // first query head of the group
   const bool ml_writer = (wave == 0) && (h == 0);
+  const int64_t chunk_rows = (int64_t)p.batch * p.hq;  // (row, head) slots per chunk
+
+  auto store_ml = [&](int chunk, float mv, float lv) {
+    const rsrc_t mlr = make_rsrc(p.part_ml + 2 * ((int64_t)chunk * chunk_rows + row_head),
+                                 (uint32_t)grp * 8u);
+    buf_store8(mlr, ml_writer ? (uint32_t)n * 8u : kParked, u32x2{f32_bits(mv), f32_bits(lv)});
+  };
 
   if constexpr (SPLIT) {
-    if (blk_begin >= blk_end) {
-      const int64_t mlh = (int64_t)chunk * p.batch * p.hq + row_head;
-      const rsrc_t mlr = make_rsrc(p.part_ml + 2 * mlh, (uint32_t)grp * 8u);
-      buf_store8(mlr, ml_writer ? (uint32_t)n * 8u : kParked,
-                 u32x2{f32_bits(-INFINITY), 0u});
-      return;
-    }
+    const int c0 = cgrp * kSplitChunks;
+    const int c1 = min(c0 + kSplitChunks, p.cmax);
+    // Chunks past the context hold empty partials (m, l) = (-inf, 0).
+    for (int cc = max(c0, nch); cc < c1; ++cc) store_ml(cc, -INFINITY, 0.0f);
+    blk_begin = c0 * kBlocksPerChunk;
+    blk_end = min(c1 * kBlocksPerChunk, nblk);
+    if (blk_begin >= blk_end) return;
   }
 
-  // Q^T operands straight from HBM; columns >= G read zero (descriptor bound).
-  QFrag<FP8> qf[G::kSteps];
+  // The group's G query rows, plus one zero row that the padding columns
+  // (n >= G) read, staged in LDS; Q^T operands are read from there per block.
   {
     const rsrc_t qr = make_rsrc(static_cast<const unsigned char*>(p.q) + row_head * G::kRowBytes,
                                 (uint32_t)(grp * G::kRowBytes));
-#pragma unroll
-    for (int st = 0; st < G::kSteps; ++st) {
-      const uint32_t off = (uint32_t)(n * G::kRowBytes + (16 * st + 8 * h) * G::kEs);
-      if constexpr (FP8) {
-        qf[st].v = buf_load8(qr, off);
-      } else {
-        qf[st].v = buf_load16(qr, off);
-      }
+    for (int x = tid; x < (grp + 1) * G::kChunks16; x += C::kThreads) {
+      const int r = x / G::kChunks16, col = x % G::kChunks16;
+      lds_store16(sQ, (uint32_t)(r * G::kQRow + col * 16),
+                  buf_load16(qr, (uint32_t)(r * G::kRowBytes + col * 16)));
     }
   }
+  const unsigned char* const qrow = sQ + min(n, grp) * G::kQRow;
 
   const float c = p.c_scale;
   f32x16 acc[1], A[1];
@@ -159,62 +173,93 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
     const unsigned char* vc = static_cast<const unsigned char*>(p.vc);
     const int32_t* table = p.page_table + (int64_t)b * p.max_pages;
     const int64_t head_off = (int64_t)g * p.head_stride;
-    PagedStager<D, FP8> stg;
-    stg.load(p, kc, vc, table, blk_begin * kBlockKeys, ctx, head_off, tid);
-    stg.store(sK, sV, tid);
+    // Element offset of a page's slot 0 for this kv head, or -1 for a page
+    // index outside the cache.
+    auto lookup = [&](int page_idx) -> int64_t {
+      const int64_t pg = table[page_idx];
+      return (pg >= 0 && pg < p.num_pages) ? pg * p.page_stride + head_off : -1;
+    };
+    const int page0 = blk_begin * kPagesPerBlock;
+    if constexpr (SPLIT) {
+      // The split workgroup's page-table entries, read once into LDS, so a
+      // block's K/V loads wait on one memory round trip instead of two.
+      const int npg = min((blk_end - blk_begin) * kPagesPerBlock,
+                          (ctx + kPageSize - 1) / kPageSize - page0);
+      for (int e = tid; e < npg; e += C::kThreads) sPage[e] = lookup(page0 + e);
+      __syncthreads();
+    }
+    auto page_base = [&](int j) -> int64_t {
+      if constexpr (SPLIT) {
+        return sPage[j / kPageSize - page0];
+      } else {
+        return lookup(j / kPageSize);
+      }
+    };
+    // Two register staging sets, used by alternate blocks: iteration blk
+    // issues the loads of block blk+2 while block blk+1's registers (loaded
+    // one iteration earlier) go to the free LDS stage, so two blocks' K/V are
+    // in flight per workgroup.
+    PagedStager<D, FP8> sa, sb;
+    sa.load(kc, vc, blk_begin * kBlockKeys, ctx, p.token_stride, tid, page_base);
+    sa.store(sK, sV, tid);
+    if (blk_begin + 1 < blk_end)
+      sb.load(kc, vc, (blk_begin + 1) * kBlockKeys, ctx, p.token_stride, tid, page_base);
     __syncthreads();
+    auto step = [&](int blk, PagedStager<D, FP8>& next1, PagedStager<D, FP8>& next2) {
+      const int cur = (blk - blk_begin) & 1;
+      if (blk + 2 < blk_end)
+        next2.load(kc, vc, (blk + 2) * kBlockKeys, ctx, p.token_stride, tid, page_base);
+      const unsigned char* ks = sK + cur * G::kKStage;
+      const unsigned char* vs = sV + cur * G::kVStage;
+      f32x16 s[2];
+      qk_scores_qrow<D, FP8>(s, qrow, ks, lane);
+      float alpha;
+      u32x4 pb[4];
+      if (kBlockKeys * (blk + 1) <= ctx) {
+        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+      } else {
+        softmax_block<true>(s, h, c, ctx - kBlockKeys * blk, m, l, alpha, pb);
+      }
+      pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
+      if (blk + 1 < blk_end) next1.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
+      __syncthreads();
+    };
     for (int blk = blk_begin; blk < blk_end;) {
       const int cend = min(blk_end, (blk / kBlocksPerChunk + 1) * kBlocksPerChunk);
       for (; blk < cend; ++blk) {
-        const int cur = (blk - blk_begin) & 1;
-        const bool more = blk + 1 < blk_end;
-        if (more) stg.load(p, kc, vc, table, (blk + 1) * kBlockKeys, ctx, head_off, tid);
-        const unsigned char* ks = sK + cur * G::kKStage;
-        const unsigned char* vs = sV + cur * G::kVStage;
-        f32x16 s[2];
-        qk_scores<D, FP8>(s, qf, ks, lane);
-        float alpha;
-        u32x4 pb[4];
-        if (kBlockKeys * (blk + 1) <= ctx) {
-          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+        if (((blk - blk_begin) & 1) == 0) {
+          step(blk, sb, sa);
         } else {
-          softmax_block<true>(s, h, c, ctx - kBlockKeys * blk, m, l, alpha, pb);
+          step(blk, sa, sb);
         }
-        pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
-        if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
-        __syncthreads();
       }
-      if constexpr (!SPLIT) {
+      const int chunk = (blk - 1) / kBlocksPerChunk;  // the chunk just completed
+      if constexpr (SPLIT) {
+        store_ml(chunk, m, l);
+        const rsrc_t ar = make_rsrc(p.part_acc + ((int64_t)chunk * chunk_rows + row_head) * D,
+                                    (uint32_t)grp * D * 4u);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * wave + 8 * q4 + 4 * h;
+          buf_store16(ar, (uint32_t)(n * D + d) * 4u,
+                      u32x4{f32_bits(acc[0][4 * q4 + 0]), f32_bits(acc[0][4 * q4 + 1]),
+                            f32_bits(acc[0][4 * q4 + 2]), f32_bits(acc[0][4 * q4 + 3])});
+        }
+      } else {
         float ca, cb;
         int mode;
         merge_stats(M, L, m, l, ca, cb, mode);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          A[0][i] = merge_elem(A[0][i], acc[0][i], mode, ca, cb);
-          acc[0][i] = 0.0f;
-        }
-        m = -INFINITY;
-        l = 0.0f;
+        for (int i = 0; i < 16; ++i) A[0][i] = merge_elem(A[0][i], acc[0][i], mode, ca, cb);
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[0][i] = 0.0f;
+      m = -INFINITY;
+      l = 0.0f;
     }
   }
 
-  if constexpr (SPLIT) {
-    const int64_t mlh = (int64_t)chunk * p.batch * p.hq + row_head;
-    const rsrc_t mlr = make_rsrc(p.part_ml + 2 * mlh, (uint32_t)grp * 8u);
-    buf_store8(mlr, ml_writer ? (uint32_t)n * 8u : kParked,
-               u32x2{f32_bits(m), f32_bits(l)});
-    const rsrc_t ar = make_rsrc(p.part_acc + mlh * D, (uint32_t)grp * D * 4u);
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = 32 * wave + 8 * q4 + 4 * h;
-      buf_store16(ar, (uint32_t)(n * D + d) * 4u,
-                  u32x4{f32_bits(acc[0][4 * q4 + 0]),
-                        f32_bits(acc[0][4 * q4 + 1]),
-                        f32_bits(acc[0][4 * q4 + 2]),
-                        f32_bits(acc[0][4 * q4 + 3])});
-    }
-  } else {
+  if constexpr (!SPLIT) {
     const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + row_head * D * 2,
                                  (uint32_t)grp * D * 2u);
     const float vd = p.v_descale;
@@ -229,21 +274,22 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
     }
     if (p.lse != nullptr) {
       const rsrc_t lr = make_rsrc(p.lse + row_head, (uint32_t)grp * 4u);
-      buf_store4(lr, ml_writer ? (uint32_t)n * 4u : kParked,
-                 f32_bits(finalize_lse(M, L)));
+      buf_store4(lr, ml_writer ? (uint32_t)n * 4u : kParked, f32_bits(finalize_lse(M, L)));
     }
   }
 }
 
 template <int D, bool FP8>
 hipError_t launch_one(const DecodeParams& p, bool split, hipStream_t stream) {
-  const long long per = (long long)p.batch * p.hkv * (split ? p.cmax : 1);
+  const long long per = (long long)p.batch * p.hkv *
+                        (split ? (p.cmax + kSplitChunks - 1) / kSplitChunks : 1);
   if (per <= 0) return hipSuccess;
   dim3 grid((unsigned)per), block(DecodeCfg<D, FP8>::kThreads);
+  const size_t qlds = (size_t)(p.group + 1) * Geom<D, FP8>::kQRow;
   if (split) {
-    hipLaunchKernelGGL((decode_kernel<D, FP8, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, FP8, true>), grid, block, qlds, stream, p);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, FP8, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, FP8, false>), grid, block, qlds, stream, p);
   }
   return hipGetLastError();
 }
