@@ -66,23 +66,36 @@ def counted_traffic(kernel: str):
     return rec["kernels"][kernel]["hbm_bytes"]
 
 
-def event_time(fn, iters: int, warmup: int):
-    """Run fn warmup + iters times; return per-call ms from HIP events recorded
-    on the current stream (the stream every launch of the library goes to)."""
+def timed(fn, steps: int, warmup: int, min_warm_s: float = 0.3):
+    """Warm up (at least `warmup` calls and about `min_warm_s` seconds of work,
+    so the GPU clocks have ramped), then run `steps` calls back to back.
+    Returns (per-call ms from HIP events recorded on the launch stream around
+    each call, wall seconds of the whole timed region between two device
+    synchronisations).  Both figures come from the same calls."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < min_warm_s:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(iters)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for a, b in evs:
         a.record(st)
         fn()
         b.record(st)
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return ms
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in evs], wall
 
 
 def prefill_workload(cfg, causal, dtype, seed=0):
@@ -114,7 +127,7 @@ def prefill_entry(name, cfg, causal, dtype, iters, warmup, peak, peak_note):
     import oracle
     inp, t = prefill_workload(cfg, causal, dtype)
     fn, _ = run_prefill_fn(inp, t, 0)
-    ms = event_time(fn, iters, warmup)
+    ms, _ = timed(fn, iters, warmup)
     flops = oracle.attention_flops(cfg["seqlens"], cfg["seqlens"], cfg["hq"], cfg["d"], causal)
     avg = sum(ms) / len(ms)
     tf = flops / (avg * 1e-3) / 1e12
@@ -165,9 +178,9 @@ def decode_entry(iters, warmup):
     def both():
         split()
         merge()
-    ms_split = event_time(split, iters, warmup)
-    ms_merge = event_time(merge, iters, warmup)
-    ms_step = event_time(both, iters, warmup)
+    ms_split, _ = timed(split, iters, warmup)
+    ms_merge, _ = timed(merge, iters, warmup)
+    ms_step, _ = timed(both, iters, warmup)
     nbytes = decode_bytes(inp)
     a_split = sum(ms_split) / iters
     a_step = sum(ms_step) / iters
@@ -264,18 +277,9 @@ def main():
     inp, t = prefill_workload(cfg, False, "bf16")
     fn, _ = run_prefill_fn(inp, t, dfa.MONOLITHIC)
     flops = oracle.attention_flops(cfg["seqlens"], cfg["seqlens"], cfg["hq"], cfg["d"], False)
-    for _ in range(args.warmup):
-        fn()
-    torch.cuda.synchronize()
-    # Per-launch kernel time from events on the launch stream.
-    ms_kernel = event_time(fn, args.steps, 0)
-    # Whole timed region: K steps between two device synchronisations.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        fn()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    # K steps timed back to back after the warm-up; HIP events around each
+    # step (on the launch stream) give the kernel time for the roofline.
+    ms_kernel, wall = timed(fn, args.steps, args.warmup)
     ms_step = wall * 1e3 / args.steps
     value = flops * args.steps / wall / 1e12
     k_avg = sum(ms_kernel) / len(ms_kernel)
@@ -284,11 +288,11 @@ def main():
     secondary = []
     if not args.no_secondary:
         secondary.append(prefill_entry("causal_gqa_varlen", synth.CAUSAL_VARLEN, True, "bf16",
-                                       10, 2, PEAK_BF16_TFLOPS, "bf16 dense MFMA"))
-        secondary.append(decode_entry(10, 2))
+                                       20, 3, PEAK_BF16_TFLOPS, "bf16 dense MFMA"))
+        secondary.append(decode_entry(20, 3))
         mixed = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
         for causal in (False, True):
-            e = prefill_entry("fp8_wide_head", synth.FP8_WIDE, causal, "fp8", 10, 2, mixed,
+            e = prefill_entry("fp8_wide_head", synth.FP8_WIDE, causal, "fp8", 20, 3, mixed,
                               "QK^T on fp8 MFMA, PV on bf16 MFMA: half the FLOPs at each peak")
             e["frac_of_bf16_peak"] = e["value"] / PEAK_BF16_TFLOPS
             secondary.append(e)

@@ -23,7 +23,7 @@ namespace {
 
 constexpr int kPageSize = 16;
 constexpr int kPagesPerBlock = kBlockKeys / kPageSize;
-constexpr int kSplitChunks = 4;  // consecutive chunks per split workgroup
+constexpr int kSplitChunks = 2;  // consecutive chunks per split workgroup
 
 template <int D, bool FP8>
 struct DecodeCfg {
@@ -195,43 +195,30 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
         return lookup(j / kPageSize);
       }
     };
-    // Two register staging sets, used by alternate blocks: iteration blk
-    // issues the loads of block blk+2 while block blk+1's registers (loaded
-    // one iteration earlier) go to the free LDS stage, so two blocks' K/V are
-    // in flight per workgroup.
-    PagedStager<D, FP8> sa, sb;
-    sa.load(kc, vc, blk_begin * kBlockKeys, ctx, p.token_stride, tid, page_base);
-    sa.store(sK, sV, tid);
-    if (blk_begin + 1 < blk_end)
-      sb.load(kc, vc, (blk_begin + 1) * kBlockKeys, ctx, p.token_stride, tid, page_base);
+    PagedStager<D, FP8> stg;
+    stg.load(kc, vc, blk_begin * kBlockKeys, ctx, p.token_stride, tid, page_base);
+    stg.store(sK, sV, tid);
     __syncthreads();
-    auto step = [&](int blk, PagedStager<D, FP8>& next1, PagedStager<D, FP8>& next2) {
-      const int cur = (blk - blk_begin) & 1;
-      if (blk + 2 < blk_end)
-        next2.load(kc, vc, (blk + 2) * kBlockKeys, ctx, p.token_stride, tid, page_base);
-      const unsigned char* ks = sK + cur * G::kKStage;
-      const unsigned char* vs = sV + cur * G::kVStage;
-      f32x16 s[2];
-      qk_scores_qrow<D, FP8>(s, qrow, ks, lane);
-      float alpha;
-      u32x4 pb[4];
-      if (kBlockKeys * (blk + 1) <= ctx) {
-        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
-      } else {
-        softmax_block<true>(s, h, c, ctx - kBlockKeys * blk, m, l, alpha, pb);
-      }
-      pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
-      if (blk + 1 < blk_end) next1.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
-      __syncthreads();
-    };
     for (int blk = blk_begin; blk < blk_end;) {
       const int cend = min(blk_end, (blk / kBlocksPerChunk + 1) * kBlocksPerChunk);
       for (; blk < cend; ++blk) {
-        if (((blk - blk_begin) & 1) == 0) {
-          step(blk, sb, sa);
+        const int cur = (blk - blk_begin) & 1;
+        const bool more = blk + 1 < blk_end;
+        if (more) stg.load(kc, vc, (blk + 1) * kBlockKeys, ctx, p.token_stride, tid, page_base);
+        const unsigned char* ks = sK + cur * G::kKStage;
+        const unsigned char* vs = sV + cur * G::kVStage;
+        f32x16 s[2];
+        qk_scores_qrow<D, FP8>(s, qrow, ks, lane);
+        float alpha;
+        u32x4 pb[4];
+        if (kBlockKeys * (blk + 1) <= ctx) {
+          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
         } else {
-          step(blk, sa, sb);
+          softmax_block<true>(s, h, c, ctx - kBlockKeys * blk, m, l, alpha, pb);
         }
+        pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
+        if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
+        __syncthreads();
       }
       const int chunk = (blk - 1) / kBlocksPerChunk;  // the chunk just completed
       if constexpr (SPLIT) {

@@ -104,13 +104,26 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5;
-  // Work decode: batch fastest, then head, then (split) chunk, then tiles from
-  // the last (heaviest under a causal mask) to the first.
+  // Work decode.  Workgroup ids are dealt round-robin to the eight XCDs
+  // (id % 8), so the head index varies fastest: with Hq a multiple of 8, XCD x
+  // owns query heads [x*Hq/8, (x+1)*Hq/8) -- contiguous GQA groups, whose K/V
+  // then stay in that XCD's L2 -- and every XCD gets an equal share of every
+  // sequence.  Then the batch, then (split) the chunk, then tiles from the last
+  // (heaviest under a causal mask) to the first.
   int id = blockIdx.x;
+  int head;
+  if (p.hq % 8 == 0) {
+    const int per = p.hq / 8;
+    const int x = id % 8;
+    id /= 8;
+    head = x * per + id % per;
+    id /= per;
+  } else {
+    head = id % p.hq;
+    id /= p.hq;
+  }
   const int b = id % p.batch;
   id /= p.batch;
-  const int head = id % p.hq;
-  id /= p.hq;
   int chunk = 0;
   if constexpr (SPLIT) {
     chunk = id % p.cmax;
