@@ -25,19 +25,20 @@ namespace detattn {
 
 namespace {
 
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, int NS = 2>
 struct PrefillCfg {
   using G = Geom<D, FP8>;
+  static constexpr int kStages = NS;  // LDS stages per K and per V
   static constexpr int kThreads = NW * kWave;
   static constexpr int kTileRows = 32 * NW;
   static constexpr int kQBytes = kTileRows * G::kQRow;
   static constexpr int kBlockChunks = kBlockKeys * G::kChunks16;  // 16-B chunks per K block
   static constexpr int kPerThread = (kBlockChunks + kThreads - 1) / kThreads;
   static constexpr int kKOff = kQBytes;
-  static constexpr int kVOff = kKOff + 2 * G::kKStage;
-  static constexpr int kLds = kVOff + 2 * G::kVStage;
-  // Q tile, the two K stages and the two V stages are disjoint byte ranges.
-  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * G::kKStage, "LDS regions overlap");
+  static constexpr int kVOff = kKOff + NS * G::kKStage;
+  static constexpr int kLds = kVOff + NS * G::kVStage;
+  // Q tile, the K stages and the V stages are disjoint byte ranges.
+  static_assert(kKOff >= kQBytes && kVOff >= kKOff + NS * G::kKStage, "LDS regions overlap");
 };
 
 __device__ __forceinline__ uint32_t extent_bytes(int64_t nrows, int64_t row_bytes,
@@ -91,10 +92,11 @@ struct KVStager {
   }
 };
 
-template <int D, bool FP8, int NW, bool SPLIT>
-__global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p) {
+template <int D, bool FP8, int NW, int NS, int WPE, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void prefill_kernel(const PrefillParams p) {
   using G = Geom<D, FP8>;
-  using C = PrefillCfg<D, FP8, NW>;
+  using C = PrefillCfg<D, FP8, NW, NS>;
   static_assert(C::kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
   constexpr int NT = G::kDTiles;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p)
     const rsrc_t kr = make_rsrc(kb, kv_ext);
     const rsrc_t vr = make_rsrc(vb, kv_ext);
 
-    KVStager<D, FP8, NW> stg;
+    KVStager<D, FP8, NW> stg;  // the staging registers do not depend on the stage count
     stg.load(kr, vr, blk_begin * kBlockKeys, kv_row_bytes, tid);
     // Q tile -> LDS (rows past the sequence read as zero).
     for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p)
     for (int blk = blk_begin; blk < blk_end;) {
       const int cend = min(blk_end, (blk / kBlocksPerChunk + 1) * kBlocksPerChunk);
       for (; blk < cend; ++blk) {
-        const int cur = (blk - blk_begin) & 1;
+        const int cur = NS == 2 ? (blk - blk_begin) & 1 : 0;
         const bool more = blk + 1 < blk_end;
         if (more) stg.load(kr, vr, (blk + 1) * kBlockKeys, kv_row_bytes, tid);
         const unsigned char* ks = sK + cur * G::kKStage;
@@ -228,8 +230,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p)
           softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
         }
         pv_accumulate<D, NT>(acc, 0, alpha, pb, vs, lane);
-        if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
-        __syncthreads();
+        if constexpr (NS == 2) {
+          if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
+          __syncthreads();
+        } else {
+          // One stage: every wave has finished reading it before it is refilled.
+          __syncthreads();
+          if (more) {
+            stg.store(sK, sV, tid);
+            __syncthreads();
+          }
+        }
       }
       if constexpr (!SPLIT) {
         // End of a 512-key chunk: fold its partial into the running total.
@@ -299,34 +310,43 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(const PrefillParams p)
   }
 }
 
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, int NS, int WPE>
 hipError_t launch_one(const PrefillParams& p, bool split, hipStream_t stream) {
   const long long per = (long long)p.batch * p.hq * p.tiles * (split ? p.cmax : 1);
   if (per <= 0) return hipSuccess;
   dim3 grid((unsigned)per), block(NW * kWave);
   if (split) {
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, NS, WPE, true>), grid, block, 0, stream, p);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, NS, WPE, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
 
-// Waves per workgroup: eight (two per SIMD, so one wave's MFMAs overlap the
-// other's softmax) up to D = 128, where a wave's registers fit in the 256
-// that two waves per SIMD leave it; four (one per SIMD) for wider heads.
+// Per (head_dim, dtype): waves per workgroup, LDS stages, and the waves per
+// SIMD the register budget targets.  Eight waves (two per SIMD, so one wave's
+// MFMAs overlap the other's softmax) up to D = 128, where a wave fits in the
+// 256 registers that leaves it; four waves (one per SIMD) for wider heads.
 template <int D, bool FP8>
-constexpr int prefill_waves() {
-  return D <= 128 ? 8 : 4;
+struct Layout {
+  static constexpr int kWaves = D <= 128 ? 8 : 4;
+  static constexpr int kStages = 2;
+  static constexpr int kWavesPerEU = D <= 128 ? 2 : 1;
+};
+
+template <int D, bool FP8>
+hipError_t launch_layout(const PrefillParams& p, bool split, hipStream_t stream) {
+  using L = Layout<D, FP8>;
+  return launch_one<D, FP8, L::kWaves, L::kStages, L::kWavesPerEU>(p, split, stream);
 }
 
 }  // namespace
 
 int prefill_tile_rows(int head_dim, bool fp8) {
   switch (head_dim) {
-    case 64: return 32 * (fp8 ? prefill_waves<64, true>() : prefill_waves<64, false>());
-    case 128: return 32 * (fp8 ? prefill_waves<128, true>() : prefill_waves<128, false>());
-    case 192: return 32 * (fp8 ? prefill_waves<192, true>() : prefill_waves<192, false>());
+    case 64: return 32 * (fp8 ? Layout<64, true>::kWaves : Layout<64, false>::kWaves);
+    case 128: return 32 * (fp8 ? Layout<128, true>::kWaves : Layout<128, false>::kWaves);
+    case 192: return 32 * (fp8 ? Layout<192, true>::kWaves : Layout<192, false>::kWaves);
     default: return 32 * 8;
   }
 }
@@ -335,14 +355,14 @@ hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, bool s
                           hipStream_t stream) {
   switch (head_dim) {
     case 64:
-      return fp8 ? launch_one<64, true, prefill_waves<64, true>()>(p, split, stream)
-                 : launch_one<64, false, prefill_waves<64, false>()>(p, split, stream);
+      return fp8 ? launch_layout<64, true>(p, split, stream)
+                 : launch_layout<64, false>(p, split, stream);
     case 128:
-      return fp8 ? launch_one<128, true, prefill_waves<128, true>()>(p, split, stream)
-                 : launch_one<128, false, prefill_waves<128, false>()>(p, split, stream);
+      return fp8 ? launch_layout<128, true>(p, split, stream)
+                 : launch_layout<128, false>(p, split, stream);
     case 192:
-      return fp8 ? launch_one<192, true, prefill_waves<192, true>()>(p, split, stream)
-                 : launch_one<192, false, prefill_waves<192, false>()>(p, split, stream);
+      return fp8 ? launch_layout<192, true>(p, split, stream)
+                 : launch_layout<192, false>(p, split, stream);
     default:
       return hipErrorInvalidValue;
   }
