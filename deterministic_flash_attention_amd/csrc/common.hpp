@@ -40,6 +40,16 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+// Direct global -> LDS load, 16 bytes per lane: lane i writes lds_seg + 16 i
+// (lds_seg is wave-uniform; it becomes M0).  A lane whose offset fails the
+// range check writes zeros, like a range-checked load into registers.  The
+// data lands asynchronously: wait_vm() before the barrier that publishes it.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, unsigned char* lds_seg, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_seg, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
@@ -74,6 +84,7 @@ __device__ __forceinline__ s16x4 lds_load_tr16(const unsigned char* lds, uint32_
 // Bits of an fp32 value.  Takes the value by copy: applied directly to an
 // ext-vector element subscript, __builtin_bit_cast reads element 0 instead.
 __device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bits_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
 }

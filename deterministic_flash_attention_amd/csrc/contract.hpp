@@ -141,6 +141,20 @@ __device__ __forceinline__ void qk_scores_qlds(f32x16 (&s)[2], const unsigned ch
   qk_scores_qrow<D, FP8>(s, qs + (lane & 31) * Geom<D, FP8>::kQRow, ks, lane);
 }
 
+// Combine a value with the one in lane ^ 32.  v_permlane32_swap exchanges the
+// upper half-wave of its first operand with the lower half-wave of its second;
+// swapping a register with itself leaves the lower half in r[0] and the upper
+// half in r[1] of every lane, so both half-waves evaluate lo (op) hi with the
+// same operand order and get the same bits.
+__device__ __forceinline__ float half_wave_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
+  return fmaxf(bits_f32(r[0]), bits_f32(r[1]));
+}
+__device__ __forceinline__ float half_wave_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f32_bits(x), f32_bits(x), false, false);
+  return bits_f32(r[0]) + bits_f32(r[1]);
+}
+
 // Online-softmax update of one lane's query column over a 64-key block.
 // rel_lim: keys at block offset >= rel_lim are masked (applied when `masked`).
 // Returns alpha for the accumulator and P^T as four bf16x8 PV operands.
@@ -181,7 +195,7 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
   float mr = fmaxf(mr0, mr1);
   step(1);
   // Phase 2: the other half-wave (lane ^ 32) holds the remaining 32 keys.
-  mr = fmaxf(mr, __shfl_xor(mr, 32));
+  mr = half_wave_max(mr);
   const float mb = mr * c;
   const float mn = fmaxf(m, mb);
   const bool empty = (mn == -INFINITY);
@@ -208,7 +222,7 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
   for (int w = 4; w >= 1; w >>= 1)
 #pragma unroll
     for (int i = 0; i < w; ++i) u[i] = u[i] + u[i + w];
-  const float rs = u[0] + __shfl_xor(u[0], 32);
+  const float rs = half_wave_sum(u[0]);
   l = l * alpha + rs;
   m = mn;
   step(6);
@@ -229,18 +243,22 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
   softmax_block(s, h, c, rel_lim, MASKED, m, l, alpha, pb, NoStep{});
 }
 
-// acc_j = acc_j * alpha + P V for the NT output tiles starting at tile dt0.
-// The V^T operand comes from the row-major bf16 V stage through the transposing
-// LDS read: lane (group G, i) gets V[16kk + 8h + 0..7][32dt + 16(G%2) + i].
-template <int D, int NT>
-__device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[NT], int dt0, float alpha,
-                                              const u32x4 (&pb)[4], const unsigned char* vs,
-                                              int lane) {
-  constexpr int kVRow = D * 2 + 64;
+// acc_j = acc_j * alpha, the first half of the accumulator update.
+template <int NT>
+__device__ __forceinline__ void rescale_acc(f32x16 (&acc)[NT], float alpha) {
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[j][i] = acc[j][i] * alpha;
+}
+
+// acc_j += P V for the NT output tiles starting at tile dt0 (acc already rescaled).
+// The V^T operand comes from the row-major bf16 V stage through the transposing
+// LDS read: lane (group G, i) gets V[16kk + 8h + 0..7][32dt + 16(G%2) + i].
+template <int D, int NT>
+__device__ __forceinline__ void pv_mfma(f32x16 (&acc)[NT], int dt0, const u32x4 (&pb)[4],
+                                        const unsigned char* vs, int lane) {
+  constexpr int kVRow = D * 2 + 64;
   const int grp = lane >> 4, li = lane & 15;
   const int h = grp >> 1;
   const int key_r = li >> 2, dq = (li & 3) * 4;
@@ -255,6 +273,15 @@ __device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[NT], int dt0, float 
       acc[j] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[kk], acc[j]);
     }
   }
+}
+
+// acc_j = acc_j * alpha + P V: both halves back to back.
+template <int D, int NT>
+__device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[NT], int dt0, float alpha,
+                                              const u32x4 (&pb)[4], const unsigned char* vs,
+                                              int lane) {
+  rescale_acc<NT>(acc, alpha);
+  pv_mfma<D, NT>(acc, dt0, pb, vs, lane);
 }
 
 // Chunk merge: fold one partial (m, l) into the running (M, L).

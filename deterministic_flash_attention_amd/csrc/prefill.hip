@@ -1,12 +1,16 @@
 // Prefill / full-sequence forward over packed variable-length sequences.
 //
 // One workgroup owns a tile of 32*NW query rows of one (sequence, query head).
-// The Q tile is staged once in its own LDS region and each wave keeps its 32
-// rows' Q^T operands in registers; K and V blocks of 64 keys stream through
-// two LDS stages that are disjoint from the Q region (the ffpa-attn fp8 D=192
-// page shows what a K stage landing in a live Q tile does).  Keys are folded in
+// The Q tile is staged once in its own LDS region, from which each wave reads
+// its 32 rows' Q^T operands; K and V blocks of 64 keys stream through two LDS
+// stages that are disjoint from the Q region (the ffpa-attn fp8 D=192 page
+// shows what a K stage landing in a live Q tile does).  Keys are folded in
 // 512-key chunks exactly as contract.hpp prescribes.
 //
+// bf16 K and V go from HBM straight into the padded LDS stages (buffer loads
+// with an LDS destination, no staging registers); fp8 goes through registers
+// because V is widened to bf16 on the way.  Block j+1 is in flight while block
+// j is computed; one workgroup barrier per block retires a stage.
 // Schedules (RL-Kernel page, section 2):
 //   monolithic  the workgroup folds every chunk of its tile in registers and
 //               stores bf16 O (and lse);
@@ -25,20 +29,20 @@ namespace detattn {
 
 namespace {
 
-template <int D, bool FP8, int NW, int NS = 2>
+template <int D, bool FP8, int NW>
 struct PrefillCfg {
   using G = Geom<D, FP8>;
-  static constexpr int kStages = NS;  // LDS stages per K and per V
+  static constexpr bool kDirect = !FP8;  // K/V staged by direct global -> LDS loads
   static constexpr int kThreads = NW * kWave;
   static constexpr int kTileRows = 32 * NW;
   static constexpr int kQBytes = kTileRows * G::kQRow;
   static constexpr int kBlockChunks = kBlockKeys * G::kChunks16;  // 16-B chunks per K block
   static constexpr int kPerThread = (kBlockChunks + kThreads - 1) / kThreads;
   static constexpr int kKOff = kQBytes;
-  static constexpr int kVOff = kKOff + NS * G::kKStage;
-  static constexpr int kLds = kVOff + NS * G::kVStage;
-  // Q tile, the K stages and the V stages are disjoint byte ranges.
-  static_assert(kKOff >= kQBytes && kVOff >= kKOff + NS * G::kKStage, "LDS regions overlap");
+  static constexpr int kVOff = kKOff + 2 * G::kKStage;
+  static constexpr int kLds = kVOff + 2 * G::kVStage;
+  // Q tile, the two K stages and the two V stages are disjoint byte ranges.
+  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * G::kKStage, "LDS regions overlap");
 };
 
 __device__ __forceinline__ uint32_t extent_bytes(int64_t nrows, int64_t row_bytes,
@@ -50,7 +54,8 @@ __device__ __forceinline__ uint32_t extent_bytes(int64_t nrows, int64_t row_byte
   return (uint32_t)e;
 }
 
-// Global -> registers -> LDS staging of one 64-key K and V block.
+// Global -> registers -> LDS staging of a 64-key K block and a 64-key V block
+// (not necessarily the same block; either may be absent, uniformly per call).
 template <int D, bool FP8, int NW>
 struct KVStager {
   using G = Geom<D, FP8>;
@@ -58,26 +63,27 @@ struct KVStager {
   u32x4 kreg[C::kPerThread];
   u32x4 vreg[C::kPerThread];
 
-  __device__ __forceinline__ void load(rsrc_t kr, rsrc_t vr, int key0, uint32_t row_bytes,
-                                       int tid) {
+  __device__ __forceinline__ void load(rsrc_t kr, int kkey0, bool kon, rsrc_t vr, int vkey0,
+                                       bool von, uint32_t row_bytes, int tid) {
 #pragma unroll
     for (int u = 0; u < C::kPerThread; ++u) {
       const int x = tid + u * C::kThreads;
       if (C::kPerThread * C::kThreads == C::kBlockChunks || x < C::kBlockChunks) {
         const int r = x / G::kChunks16, col = x % G::kChunks16;
-        const uint32_t off = (uint32_t)(key0 + r) * row_bytes + (uint32_t)col * 16u;
-        kreg[u] = buf_load16(kr, off);
-        vreg[u] = buf_load16(vr, off);
+        if (kon) kreg[u] = buf_load16(kr, (uint32_t)(kkey0 + r) * row_bytes + (uint32_t)col * 16u);
+        if (von) vreg[u] = buf_load16(vr, (uint32_t)(vkey0 + r) * row_bytes + (uint32_t)col * 16u);
       }
     }
   }
-  __device__ __forceinline__ void store(unsigned char* ks, unsigned char* vs, int tid) const {
+  __device__ __forceinline__ void store(unsigned char* ks, bool kon, unsigned char* vs, bool von,
+                                        int tid) const {
 #pragma unroll
     for (int u = 0; u < C::kPerThread; ++u) {
       const int x = tid + u * C::kThreads;
       if (C::kPerThread * C::kThreads == C::kBlockChunks || x < C::kBlockChunks) {
         const int r = x / G::kChunks16, col = x % G::kChunks16;
-        lds_store16(ks, (uint32_t)(r * G::kKRow + col * 16), kreg[u]);
+        if (kon) lds_store16(ks, (uint32_t)(r * G::kKRow + col * 16), kreg[u]);
+        if (!von) continue;
         if constexpr (FP8) {
           const u32x2 a = e4m3x4_to_bf16x4(vreg[u][0]), b = e4m3x4_to_bf16x4(vreg[u][1]);
           const u32x2 c = e4m3x4_to_bf16x4(vreg[u][2]), d = e4m3x4_to_bf16x4(vreg[u][3]);
@@ -92,11 +98,57 @@ struct KVStager {
   }
 };
 
-template <int D, bool FP8, int NW, int NS, int WPE, bool SPLIT>
+// Direct staging of one bf16 K block and one V block into their padded stages.
+// A stage is a whole number of 1 KB segments; one wave instruction fills one
+// segment, lane i the 16-byte slot i of it.  A slot is a 16-byte chunk of a
+// K/V row or a row's padding; padding lanes load from a parked offset, which
+// the range check turns into zeros.  Rows past the sequence read as zeros.
+template <int D, int NW>
+struct DirectStager {
+  using G = Geom<D, false>;
+  static constexpr int kKSlots = G::kKRow / 16;  // slots per padded row = segments per stage
+  static constexpr int kVSlots = G::kVRow / 16;
+  static constexpr int kKPer = (kKSlots + NW - 1) / NW;  // segments per wave
+  static constexpr int kVPer = (kVSlots + NW - 1) / NW;
+  static_assert(G::kKRow % 16 == 0 && G::kVRow % 16 == 0, "padded rows must be whole slots");
+  static_assert(kBlockKeys == 64 && kKSlots * 1024 == G::kKStage && kVSlots * 1024 == G::kVStage,
+                "a stage must be whole 1 KB segments");
+  uint32_t koff[kKPer];  // this lane's byte offset inside a block, per segment of this wave
+  uint32_t voff[kVPer];
+
+  static __device__ __forceinline__ uint32_t slot_offset(int seg, int lane, int slots,
+                                                         uint32_t row_bytes) {
+    const int s = 64 * seg + lane, row = s / slots, c = s % slots;
+    return c < G::kChunks16 ? (uint32_t)row * row_bytes + 16u * (uint32_t)c : kParked;
+  }
+  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes) {
+#pragma unroll
+    for (int u = 0; u < kKPer; ++u) koff[u] = slot_offset(wave + u * NW, lane, kKSlots, row_bytes);
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) voff[u] = slot_offset(wave + u * NW, lane, kVSlots, row_bytes);
+  }
+  // blk_off = first key of the block times the row stride (below 2^31, so a
+  // parked offset plus it stays out of range without wrapping).
+  __device__ __forceinline__ void issue(rsrc_t kr, rsrc_t vr, uint32_t blk_off, unsigned char* ks,
+                                        unsigned char* vs, int wave) const {
+#pragma unroll
+    for (int u = 0; u < kKPer; ++u) {
+      const int seg = wave + u * NW;
+      if (kKPer * NW == kKSlots || seg < kKSlots) buf_load16_lds(kr, ks + seg * 1024, koff[u] + blk_off);
+    }
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) {
+      const int seg = wave + u * NW;
+      if (kVPer * NW == kVSlots || seg < kVSlots) buf_load16_lds(vr, vs + seg * 1024, voff[u] + blk_off);
+    }
+  }
+};
+
+template <int D, bool FP8, int NW, int WPE, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void prefill_kernel(const PrefillParams p) {
   using G = Geom<D, FP8>;
-  using C = PrefillCfg<D, FP8, NW, NS>;
+  using C = PrefillCfg<D, FP8, NW>;
   static_assert(C::kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
   constexpr int NT = G::kDTiles;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
@@ -199,64 +251,79 @@ void prefill_kernel(const PrefillParams p) {
     const rsrc_t kr = make_rsrc(kb, kv_ext);
     const rsrc_t vr = make_rsrc(vb, kv_ext);
 
-    KVStager<D, FP8, NW> stg;  // the staging registers do not depend on the stage count
-    stg.load(kr, vr, blk_begin * kBlockKeys, kv_row_bytes, tid);
+    const int n = blk_end - blk_begin;
+    const int wv = uniform(wave);
+    DirectStager<D, NW> dst;
+    KVStager<D, FP8, NW> rst;
+    if constexpr (C::kDirect) {
+      dst.init(wv, lane, kv_row_bytes);
+      dst.issue(kr, vr, (uint32_t)(blk_begin * kBlockKeys) * kv_row_bytes, sK, sV, wv);
+    } else {
+      rst.load(kr, blk_begin * kBlockKeys, true, vr, blk_begin * kBlockKeys, true, kv_row_bytes, tid);
+    }
     // Q tile -> LDS (rows past the sequence read as zero).
     for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
       const int r = x / G::kChunks16, col = x % G::kChunks16;
       lds_store16(sQ, (uint32_t)(r * G::kQRow + col * 16),
                   buf_load16(qr, (uint32_t)(r0 + r) * q_row_bytes + (uint32_t)col * 16u));
     }
-    stg.store(sK, sV, tid);
+    if constexpr (C::kDirect) {
+      wait_vm();
+    } else {
+      rst.store(sK, true, sV, true, tid);
+    }
     __syncthreads();
 
     const unsigned char* const sQw = sQ + (32 * wave) * G::kQRow;  // this wave's Q rows
-
-    for (int blk = blk_begin; blk < blk_end;) {
-      const int cend = min(blk_end, (blk / kBlocksPerChunk + 1) * kBlocksPerChunk);
-      for (; blk < cend; ++blk) {
-        const int cur = NS == 2 ? (blk - blk_begin) & 1 : 0;
-        const bool more = blk + 1 < blk_end;
-        if (more) stg.load(kr, vr, (blk + 1) * kBlockKeys, kv_row_bytes, tid);
-        const unsigned char* ks = sK + cur * G::kKStage;
-        const unsigned char* vs = sV + cur * G::kVStage;
-        f32x16 s[2];
-        qk_scores_qlds<D, FP8>(s, sQw, ks, lane);
-        float alpha;
-        u32x4 pb[4];
-        if (kBlockKeys * (blk + 1) <= kfull) {
-          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+    for (int j = 0; j < n; ++j) {
+      const int blk = blk_begin + j, cur = j & 1;
+      const bool more = j + 1 < n;
+      // Block j+1 into the other stage; its previous block was retired by the
+      // barrier that ended block j-1.
+      if (more) {
+        if constexpr (C::kDirect) {
+          dst.issue(kr, vr, (uint32_t)((blk + 1) * kBlockKeys) * kv_row_bytes,
+                    sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, wv);
         } else {
-          softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
-        }
-        pv_accumulate<D, NT>(acc, 0, alpha, pb, vs, lane);
-        if constexpr (NS == 2) {
-          if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
-          __syncthreads();
-        } else {
-          // One stage: every wave has finished reading it before it is refilled.
-          __syncthreads();
-          if (more) {
-            stg.store(sK, sV, tid);
-            __syncthreads();
-          }
+          rst.load(kr, (blk + 1) * kBlockKeys, true, vr, (blk + 1) * kBlockKeys, true, kv_row_bytes,
+                   tid);
         }
       }
+      f32x16 s[2];
+      qk_scores_qlds<D, FP8>(s, sQw, sK + cur * G::kKStage, lane);
+      float alpha;
+      u32x4 pb[4];
+      if (kBlockKeys * (blk + 1) <= kfull) {
+        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+      } else {
+        softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
+      }
+      pv_accumulate<D, NT>(acc, 0, alpha, pb, sV + cur * G::kVStage, lane);
       if constexpr (!SPLIT) {
-        // End of a 512-key chunk: fold its partial into the running total.
-        float ca, cb;
-        int mode;
-        merge_stats(M, L, m, l, ca, cb, mode);
+        if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) {
+          // End of a 512-key chunk: fold its partial into the running total.
+          float ca, cb;
+          int mode;
+          merge_stats(M, L, m, l, ca, cb, mode);
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+          for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            A[j][i] = merge_elem(A[j][i], acc[j][i], mode, ca, cb);
-            acc[j][i] = 0.0f;
-          }
-        m = -INFINITY;
-        l = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+              A[t][i] = merge_elem(A[t][i], acc[t][i], mode, ca, cb);
+              acc[t][i] = 0.0f;
+            }
+          m = -INFINITY;
+          l = 0.0f;
+        }
       }
+      if (more) {
+        if constexpr (C::kDirect) {
+          wait_vm();
+        } else {
+          rst.store(sK + (cur ^ 1) * G::kKStage, true, sV + (cur ^ 1) * G::kVStage, true, tid);
+        }
+      }
+      __syncthreads();
     }
   }
 
@@ -310,34 +377,33 @@ void prefill_kernel(const PrefillParams p) {
   }
 }
 
-template <int D, bool FP8, int NW, int NS, int WPE>
+template <int D, bool FP8, int NW, int WPE>
 hipError_t launch_one(const PrefillParams& p, bool split, hipStream_t stream) {
   const long long per = (long long)p.batch * p.hq * p.tiles * (split ? p.cmax : 1);
   if (per <= 0) return hipSuccess;
   dim3 grid((unsigned)per), block(NW * kWave);
   if (split) {
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, NS, WPE, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, true>), grid, block, 0, stream, p);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, NS, WPE, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
 
-// Per (head_dim, dtype): waves per workgroup, LDS stages, and the waves per
-// SIMD the register budget targets.  Eight waves (two per SIMD, so one wave's
-// MFMAs overlap the other's softmax) up to D = 128, where a wave fits in the
-// 256 registers that leaves it; four waves (one per SIMD) for wider heads.
+// Per (head_dim, dtype): waves per workgroup and the waves per SIMD the
+// register budget targets.  Eight waves (two per SIMD, so one wave's MFMAs can
+// fill the other's gaps) up to D = 128, where a wave fits in the 256 registers
+// that leaves it; four waves (one per SIMD) for wider heads.
 template <int D, bool FP8>
 struct Layout {
   static constexpr int kWaves = D <= 128 ? 8 : 4;
-  static constexpr int kStages = 2;
   static constexpr int kWavesPerEU = D <= 128 ? 2 : 1;
 };
 
 template <int D, bool FP8>
 hipError_t launch_layout(const PrefillParams& p, bool split, hipStream_t stream) {
   using L = Layout<D, FP8>;
-  return launch_one<D, FP8, L::kWaves, L::kStages, L::kWavesPerEU>(p, split, stream);
+  return launch_one<D, FP8, L::kWaves, L::kWavesPerEU>(p, split, stream);
 }
 
 }  // namespace
