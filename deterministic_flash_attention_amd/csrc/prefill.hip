@@ -9,8 +9,11 @@
 //
 // bf16 K and V go from HBM straight into the padded LDS stages (buffer loads
 // with an LDS destination, no staging registers); fp8 goes through registers
-// because V is widened to bf16 on the way.  Block j+1 is in flight while block
-// j is computed; one workgroup barrier per block retires a stage.
+// because V is widened to bf16 on the way.  With eight bf16 waves the two
+// halves of the workgroup ping-pong (one in its MFMA phase while the other
+// runs its softmax, two barriers per block); otherwise every wave runs the
+// block in lockstep with block j+1 in flight and one barrier per block.
+//
 // Schedules (RL-Kernel page, section 2):
 //   monolithic  the workgroup folds every chunk of its tile in registers and
 //               stores bf16 O (and lse);
@@ -129,6 +132,20 @@ struct DirectStager {
   }
   // blk_off = first key of the block times the row stride (below 2^31, so a
   // parked offset plus it stays out of range without wrapping).
+  __device__ __forceinline__ void issue_k(rsrc_t kr, uint32_t blk_off, unsigned char* ks, int wave) const {
+#pragma unroll
+    for (int u = 0; u < kKPer; ++u) {
+      const int seg = wave + u * NW;
+      if (kKPer * NW == kKSlots || seg < kKSlots) buf_load16_lds(kr, ks + seg * 1024, koff[u] + blk_off);
+    }
+  }
+  __device__ __forceinline__ void issue_v(rsrc_t vr, uint32_t blk_off, unsigned char* vs, int wave) const {
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) {
+      const int seg = wave + u * NW;
+      if (kVPer * NW == kVSlots || seg < kVSlots) buf_load16_lds(vr, vs + seg * 1024, voff[u] + blk_off);
+    }
+  }
   __device__ __forceinline__ void issue(rsrc_t kr, rsrc_t vr, uint32_t blk_off, unsigned char* ks,
                                         unsigned char* vs, int wave) const {
 #pragma unroll
@@ -251,6 +268,90 @@ void prefill_kernel(const PrefillParams p) {
     const rsrc_t kr = make_rsrc(kb, kv_ext);
     const rsrc_t vr = make_rsrc(vb, kv_ext);
 
+    if constexpr (C::kDirect && NW == 8) {
+    // Ping-pong (bf16 staged directly, two waves per SIMD).  Each wave
+    // alternates an MFMA phase (P V of block j-1, then S_j = K_j Q^T) and a
+    // VALU phase (the softmax update of block j and the rescale of acc), one
+    // barrier after each.  The second half of the waves (w >= NW/2, which
+    // shares SIMDs with the first half: wave w and w+4 sit on one SIMD) runs
+    // one phase behind -- one extra barrier at the start, the first half one
+    // at the end -- so each SIMD holds one wave of each phase.
+    //
+    // Staging event e loads K block e+1 into K stage (e+1)%2 and V block e
+    // into V stage e%2 (blocks relative to blk_begin), each wave its own
+    // segments.  The first half performs event j in its VALU phase j, the
+    // second half event j+1 (events up to the lag in the prologue); a wave's
+    // loads land before the barrier that ends the phase that issued them.
+    // In barrier slots (first half: MFMA phase j = slot 2j, VALU phase j =
+    // slot 2j+1; second half one slot later), K_j is read in slots 2j, 2j+1
+    // and written in slots 2j-2, 2j-1; V_j is read in 2j+2, 2j+3 and written
+    // in 2j, 2j+1: every write falls after the last read of the block two
+    // earlier in the same stage and before the first read of its own block.
+    const int n = blk_end - blk_begin;
+    const int wv = uniform(wave);
+    const int lag = wv >= NW / 2 ? 1 : 0;
+    DirectStager<D, NW> dst;
+    dst.init(wv, lane, kv_row_bytes);
+    auto key_off = [&](int blk) { return (uint32_t)(blk * kBlockKeys) * kv_row_bytes; };
+    // event e: K block e+1 -> K stage (e+1)&1, V block e -> V stage e&1 (relative blocks)
+    auto event = [&](int e) {
+      if (e + 1 < n) dst.issue_k(kr, key_off(blk_begin + e + 1), sK + ((e + 1) & 1) * G::kKStage, wv);
+      if (e >= 0 && e < n) dst.issue_v(vr, key_off(blk_begin + e), sV + (e & 1) * G::kVStage, wv);
+    };
+    event(-1);
+    if (lag) event(0);
+    for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
+      const int r = x / G::kChunks16, col = x % G::kChunks16;
+      lds_store16(sQ, (uint32_t)(r * G::kQRow + col * 16),
+                  buf_load16(qr, (uint32_t)(r0 + r) * q_row_bytes + (uint32_t)col * 16u));
+    }
+    wait_vm();
+    __syncthreads();
+    if (lag) __syncthreads();
+    const unsigned char* const sQw = sQ + (32 * wave) * G::kQRow;
+    auto fold_chunk = [&]() {
+      float ca, cb;
+      int mode;
+      merge_stats(M, L, m, l, ca, cb, mode);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          A[t][i] = merge_elem(A[t][i], acc[t][i], mode, ca, cb);
+          acc[t][i] = 0.0f;
+        }
+      m = -INFINITY;
+      l = 0.0f;
+    };
+    u32x4 pb[4];
+    for (int j = 0; j < n; ++j) {
+      const int blk = blk_begin + j;
+      __builtin_amdgcn_s_setprio(2);  // MFMA phase ahead of the other half's VALU
+      if (j > 0) {
+        pv_mfma<D, NT>(acc, 0, pb, sV + ((j - 1) & 1) * G::kVStage, lane);
+        if constexpr (!SPLIT) {
+          if (blk % kBlocksPerChunk == 0) fold_chunk();
+        }
+      }
+      f32x16 s[2];
+      qk_scores_qlds<D, FP8>(s, sQw, sK + (j & 1) * G::kKStage, lane);
+      __syncthreads();
+      __builtin_amdgcn_s_setprio(0);
+      event(j + lag);
+      float alpha;
+      if (kBlockKeys * (blk + 1) <= kfull) {
+        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+      } else {
+        softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
+      }
+      rescale_acc<NT>(acc, alpha);
+      wait_vm();
+      __syncthreads();
+    }
+    pv_mfma<D, NT>(acc, 0, pb, sV + ((n - 1) & 1) * G::kVStage, lane);
+    if constexpr (!SPLIT) fold_chunk();
+    if (!lag) __syncthreads();
+      } else {
     const int n = blk_end - blk_begin;
     const int wv = uniform(wave);
     DirectStager<D, NW> dst;
@@ -325,6 +426,7 @@ void prefill_kernel(const PrefillParams p) {
       }
       __syncthreads();
     }
+      }
   }
 
   if constexpr (SPLIT) {
