@@ -156,22 +156,12 @@ __device__ __forceinline__ float half_wave_sum(float x) {
 }
 
 // Online-softmax update of one lane's query column over a 64-key block.
-// rel_lim: keys at block offset >= rel_lim are masked (applied when `masked`).
+// rel_lim: keys at block offset >= rel_lim are masked (MASKED blocks only).
 // Returns alpha for the accumulator and P^T as four bf16x8 PV operands.
-//
-// The update runs as eight phases in a fixed order; after phase k it calls
-// step(k).  Prefill passes a step that issues part of the next block's QK^T
-// MFMAs, so the matrix core works while the VALU runs these phases; decode
-// passes a step that does nothing.  The arithmetic on each lane's values is
-// the same sequence either way.
-struct NoStep {
-  __device__ __forceinline__ void operator()(int) const {}
-};
-
-template <typename Step>
+template <bool MASKED>
 __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float c, int rel_lim,
-                                              bool masked, float& m, float& l, float& alpha,
-                                              u32x4 (&pb)[4], Step&& step) {
+                                              float& m, float& l, float& alpha,
+                                              u32x4 (&pb)[4]) {
   // Phases 0-1: mask by select and row max on the raw dot products.  fl(c*s)
   // is monotonic in s for c > 0, so fl(c * max s) is exactly the max of the
   // scaled scores.
@@ -180,20 +170,18 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float v = s[0][i];
-    if (masked) v = (score_key(0, i, h) < rel_lim) ? v : -INFINITY;
+    if (MASKED) v = (score_key(0, i, h) < rel_lim) ? v : -INFINITY;
     x[0][i] = v;
     mr0 = fmaxf(mr0, v);
   }
-  step(0);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float v = s[1][i];
-    if (masked) v = (score_key(1, i, h) < rel_lim) ? v : -INFINITY;
+    if (MASKED) v = (score_key(1, i, h) < rel_lim) ? v : -INFINITY;
     x[1][i] = v;
     mr1 = fmaxf(mr1, v);
   }
   float mr = fmaxf(mr0, mr1);
-  step(1);
   // Phase 2: the other half-wave (lane ^ 32) holds the remaining 32 keys.
   mr = half_wave_max(mr);
   const float mb = mr * c;
@@ -201,15 +189,12 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
   const bool empty = (mn == -INFINITY);
   const float nms = empty ? 0.0f : -mn;
   alpha = empty ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
-  step(2);
   // Phases 3-4: p = exp2(c * s - m'), product and difference in one explicit
   // fused multiply-add (one rounding); masked scores are -inf and give p = 0.
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[0][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[0][i], c, nms));
-  step(3);
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[1][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[1][i], c, nms));
-  step(4);
   // Phases 5-6: row-sum tree: pair the two key tiles, halve 16 -> 1, then add
   // the other half-wave's sum.
   float u[16];
@@ -217,7 +202,6 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
   for (int i = 0; i < 16; ++i) u[i] = x[0][i] + x[1][i];
 #pragma unroll
   for (int i = 0; i < 8; ++i) u[i] = u[i] + u[i + 8];
-  step(5);
 #pragma unroll
   for (int w = 4; w >= 1; w >>= 1)
 #pragma unroll
@@ -225,7 +209,6 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
   const float rs = half_wave_sum(u[0]);
   l = l * alpha + rs;
   m = mn;
-  step(6);
   // Phase 7: P to bf16 (round to nearest even), packed as the PV B operand.
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -233,14 +216,6 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
 #pragma unroll
     for (int e = 0; e < 4; ++e) pb[kk][e] = pack_bf16x2(x[t][b + 2 * e], x[t][b + 2 * e + 1]);
   }
-  step(7);
-}
-
-template <bool MASKED>
-__device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float c, int rel_lim,
-                                              float& m, float& l, float& alpha,
-                                              u32x4 (&pb)[4]) {
-  softmax_block(s, h, c, rel_lim, MASKED, m, l, alpha, pb, NoStep{});
 }
 
 // acc_j = acc_j * alpha, the first half of the accumulator update.
