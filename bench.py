@@ -201,6 +201,41 @@ def decode_entry(iters, warmup):
     }
 
 
+def extend_entry(iters, warmup):
+    """The mixed prefill / extend / decode batch over a paged cache, one
+    monolithic launch of attn_paged_extend_fwd per step."""
+    import torch
+    import deterministic_flash_attention_amd as dfa
+    import oracle
+    import synth
+    cfg = synth.MIXED_EXTEND
+    inp = synth.extend_inputs(0, cfg["ctx_lens"], cfg["q_lens"], cfg["hq"], cfg["hkv"], cfg["d"],
+                              spare_pages=cfg["spare_pages"], poison=False)
+    dev = torch.device("cuda")
+    q, cq = inp.q.to(dev), inp.cu_seqlens_q.to(dev)
+    kc, vc = inp.k_cache.to(dev), inp.v_cache.to(dev)
+    pt, cl = inp.page_table.to(dev), inp.context_lens.to(dev)
+    o = torch.empty_like(q)
+    mq, mc = max(inp.q_lens), max(inp.ctx_lens)
+
+    def fn():
+        dfa.attn_paged_extend_fwd(q, cq, kc, vc, pt, cl, mq, mc, inp.scale, True, dfa.MONOLITHIC,
+                                  o=o)
+    ms, _ = timed(fn, iters, warmup)
+    flops = oracle.attention_flops(inp.q_lens, inp.ctx_lens, cfg["hq"], cfg["d"], True)
+    avg = sum(ms) / len(ms)
+    tf = flops / (avg * 1e-3) / 1e12
+    return {
+        "workload": "mixed_paged_extend", "causal": True, "dtype": "bf16",
+        "ctx_lens": inp.ctx_lens, "q_lens": inp.q_lens, "hq": cfg["hq"], "hkv": cfg["hkv"],
+        "d": cfg["d"], "flop": flops, "ms_mean": avg, "ms_min": min(ms), "value": tf,
+        "unit": "TFLOP/s",
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "prefill_kernel<128, bf16, paged, monolithic>"},
+    }
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The fp64 oracle on a bounded row sample of the dense workload: as many
     query rows as fit about target_s seconds, all 32 heads, every key."""
@@ -290,6 +325,7 @@ def main():
         secondary.append(prefill_entry("causal_gqa_varlen", synth.CAUSAL_VARLEN, True, "bf16",
                                        20, 3, PEAK_BF16_TFLOPS, "bf16 dense MFMA"))
         secondary.append(decode_entry(20, 3))
+        secondary.append(extend_entry(20, 3))
         mixed = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
         for causal in (False, True):
             e = prefill_entry("fp8_wide_head", synth.FP8_WIDE, causal, "fp8", 20, 3, mixed,

@@ -1,10 +1,11 @@
 """Python binding of libdetattn.so: argument marshalling only.
 
 The functions named like the C entry points (``attn_prefill_fwd``,
-``attn_decode_split_fwd``, ``attn_chunk_merge``, ``attn_partials_bytes``,
-``attn_num_chunks``, ``attn_status_str``) take torch tensors that already live
-on the GPU, pass their device pointers and sizes to the C ABI and raise
-``DetAttnError`` on a non-zero status.  ``prefill`` and ``decode`` additionally
+``attn_decode_split_fwd``, ``attn_paged_extend_fwd``, ``attn_chunk_merge``,
+``attn_partials_bytes``, ``attn_num_chunks``, ``attn_status_str``) take torch
+tensors that already live on the GPU, pass their device pointers and sizes to
+the C ABI and raise ``DetAttnError`` on a non-zero status.  ``prefill``,
+``decode`` and ``paged_extend`` additionally
 allocate the outputs (and the partials of the split schedule) with torch and
 chain the split and merge launches on the current stream.  Every step of the
 computation runs in the HIP kernels of the library; there is no fallback: if the
@@ -22,8 +23,8 @@ import torch
 __all__ = [
     "DetAttnError", "BF16", "FP8_E4M3", "MONOLITHIC", "SPLIT", "BLOCK_KEYS", "CHUNK_KEYS",
     "PAGE_SIZE", "library_path", "load_library", "attn_status_str", "attn_num_chunks",
-    "attn_partials_bytes", "attn_prefill_fwd", "attn_decode_split_fwd", "attn_chunk_merge",
-    "prefill", "decode",
+    "attn_partials_bytes", "attn_prefill_fwd", "attn_decode_split_fwd", "attn_paged_extend_fwd",
+    "attn_chunk_merge", "prefill", "decode", "paged_extend",
 ]
 
 BF16, FP8_E4M3 = 0, 1
@@ -71,6 +72,11 @@ def load_library() -> ctypes.CDLL:
                                           c_f32, c_f32, c_f32, c_f32, c_i32, c_p, c_sz, c_p, c_p,
                                           c_p]
     lib.attn_decode_split_fwd.restype = ctypes.c_int
+    lib.attn_paged_extend_fwd.argtypes = [c_i32, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64,
+                                          c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i64, c_i32,
+                                          c_i32, c_i32, c_i32, c_f32, c_i32, c_f32, c_f32, c_f32,
+                                          c_i32, c_p, c_p, c_p, c_sz, c_p]
+    lib.attn_paged_extend_fwd.restype = ctypes.c_int
     lib.attn_chunk_merge.argtypes = [c_p, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p]
     lib.attn_chunk_merge.restype = ctypes.c_int
     _LIB = lib
@@ -152,6 +158,25 @@ def attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_con
     _check("attn_decode_split_fwd", st)
 
 
+def attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
+                          max_seqlen_q: int, max_context_len: int, softmax_scale: float,
+                          causal: bool, schedule: int = MONOLITHIC, o=None, lse=None,
+                          partials=None, descales=(1.0, 1.0, 1.0), stream=None) -> None:
+    """Mirror of the C ``attn_paged_extend_fwd`` for caches shaped
+    [num_pages, 16, Hkv, D] (contiguous)."""
+    lib = load_library()
+    npages, psize, hkv, d = k_cache.shape
+    st = lib.attn_paged_extend_fwd(
+        _dtype_code(q), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache), int(npages),
+        int(psize * hkv * d), int(hkv * d), int(d), _ptr(page_table), int(page_table.shape[1]),
+        _ptr(context_lens), int(cu_seqlens_q.numel() - 1), int(max_seqlen_q),
+        int(max_context_len), int(q.shape[0]), int(psize), int(q.shape[1]), int(hkv), int(d),
+        float(softmax_scale), int(bool(causal)), float(descales[0]), float(descales[1]),
+        float(descales[2]), int(schedule), _ptr(o), _ptr(lse), _ptr(partials),
+        0 if partials is None else partials.numel() * partials.element_size(), _stream(stream))
+    _check("attn_paged_extend_fwd", st)
+
+
 def attn_chunk_merge(partials, rows: int, num_heads_q: int, max_chunks: int, head_dim: int,
                      o, lse=None, v_descale: float = 1.0, stream=None) -> None:
     """Mirror of the C ``attn_chunk_merge``."""
@@ -217,4 +242,30 @@ def decode(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
         attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len,
                               softmax_scale, MONOLITHIC, o=o, lse=lse, descales=descales,
                               stream=stream)
+    return (o, lse) if return_lse else o
+
+
+def paged_extend(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens, max_seqlen_q: int,
+                 max_context_len: int, causal: bool, softmax_scale: Optional[float] = None,
+                 schedule: int = MONOLITHIC, descales=(1.0, 1.0, 1.0),
+                 out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+    """Mixed prefill / extend / decode batch over a paged KV cache; returns O
+    (bf16) and optionally lse.  Sequence b's rows are its last
+    cu_seqlens_q[b+1] - cu_seqlens_q[b] tokens of context_lens[b]."""
+    tq, hq, d = q.shape
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    o = out if out is not None else torch.empty(tq, hq, d, dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty(tq, hq, dtype=torch.float32, device=q.device) if return_lse else None
+    if schedule == SPLIT:
+        cmax = attn_num_chunks(max_context_len)
+        part = _new_partials(tq, hq, cmax, d, q.device)
+        attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
+                              max_seqlen_q, max_context_len, softmax_scale, causal, SPLIT,
+                              partials=part, descales=descales, stream=stream)
+        attn_chunk_merge(part, tq, hq, cmax, d, o, lse, v_descale=descales[2], stream=stream)
+    else:
+        attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
+                              max_seqlen_q, max_context_len, softmax_scale, causal, MONOLITHIC,
+                              o=o, lse=lse, descales=descales, stream=stream)
     return (o, lse) if return_lse else o

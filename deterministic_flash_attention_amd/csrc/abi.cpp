@@ -118,7 +118,80 @@ da_status attn_prefill_fwd(int32_t dtype, const void* q, const void* k, const vo
   p.causal = causal;
   p.c_scale = score_constant(softmax_scale, q_descale, k_descale);
   p.v_descale = v_descale;
-  const hipError_t e = detattn::launch_prefill(p, head_dim, dtype == DA_FP8_E4M3, split,
+  const hipError_t e = detattn::launch_prefill(p, head_dim, dtype == DA_FP8_E4M3, split, false,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ELAUNCH;
+}
+
+da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_seqlens_q,
+                                const void* k_cache, const void* v_cache, int64_t num_pages,
+                                int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                                const int32_t* page_table, int32_t max_pages_per_seq,
+                                const int32_t* context_lens, int32_t batch, int32_t max_seqlen_q,
+                                int32_t max_context_len, int64_t total_q, int32_t page_size,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                float softmax_scale, int32_t causal, float q_descale,
+                                float k_descale, float v_descale, int32_t schedule, void* o,
+                                float* lse, float* partials, size_t partials_bytes, void* stream) {
+  if (dtype != DA_BF16 && dtype != DA_FP8_E4M3) return DA_EINVAL;
+  if (schedule != DA_MONOLITHIC && schedule != DA_SPLIT) return DA_EINVAL;
+  if (causal != 0 && causal != 1) return DA_EINVAL;
+  if (batch < 0 || max_seqlen_q < 0 || max_context_len < 0 || total_q < 0) return DA_EINVAL;
+  if (max_pages_per_seq <= 0 || num_pages <= 0) return DA_EINVAL;
+  if (page_stride <= 0 || token_stride <= 0 || head_stride <= 0) return DA_EINVAL;
+  if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return DA_EINVAL;
+  if (page_size != DA_PAGE_SIZE) return DA_EUNSUPPORTED;
+  if (!supported_dim(head_dim)) return DA_EUNSUPPORTED;
+  if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * DA_PAGE_SIZE) return DA_EINVAL;
+  if (!finite_pos(softmax_scale)) return DA_EINVAL;
+  if (!check_descales(dtype, q_descale, k_descale, v_descale)) return DA_EINVAL;
+  const bool split = schedule == DA_SPLIT;
+  const int es = dtype == DA_FP8_E4M3 ? 1 : 2;
+  if (!q || !cu_seqlens_q || !k_cache || !v_cache || !page_table || !context_lens) return DA_EINVAL;
+  if (!aligned(q, 16) || !aligned(cu_seqlens_q, 4) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(page_table, 4) || !aligned(context_lens, 4))
+    return DA_EINVAL;
+  if ((page_stride * es) % 16 || (token_stride * es) % 16 || (head_stride * es) % 16) return DA_EINVAL;
+  if (!split && (!o || !aligned(o, 16) || (lse && !aligned(lse, 4)))) return DA_EINVAL;
+  if (split && (!partials || !aligned(partials, 16))) return DA_EINVAL;
+
+  const int tile = detattn::prefill_tile_rows(head_dim, dtype == DA_FP8_E4M3);
+  if (((int64_t)max_seqlen_q + tile) * num_heads_q * head_dim * 4 > kMaxOffset) return DA_EUNSUPPORTED;
+  const int32_t tiles = (int32_t)((max_seqlen_q + tile - 1) / tile);
+  const int32_t cmax = chunks_for(max_context_len);
+  if ((int64_t)batch * num_heads_q * tiles * (split ? cmax : 1) > kMaxOffset) return DA_EUNSUPPORTED;
+  if (split && partials_bytes < partials_bytes_or_max(total_q, num_heads_q, cmax, head_dim))
+    return DA_EWORKSPACE;
+  if (batch == 0 || tiles == 0 || (split && cmax == 0)) return DA_OK;
+
+  detattn::PrefillParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = nullptr;
+  p.o = o;
+  p.lse = lse;
+  p.part_acc = partials;
+  p.part_ml = partials ? partials + (size_t)cmax * total_q * num_heads_q * head_dim : nullptr;
+  p.total_q = total_q;
+  p.total_k = 0;
+  p.batch = batch;
+  p.hq = num_heads_q;
+  p.hkv = num_heads_kv;
+  p.tiles = tiles;
+  p.cmax = cmax;
+  p.causal = causal;
+  p.c_scale = score_constant(softmax_scale, q_descale, k_descale);
+  p.v_descale = v_descale;
+  p.page_table = page_table;
+  p.ctx_lens = context_lens;
+  p.num_pages = num_pages;
+  p.page_stride = page_stride;
+  p.token_stride = token_stride;
+  p.head_stride = head_stride;
+  p.max_pages = max_pages_per_seq;
+  const hipError_t e = detattn::launch_prefill(p, head_dim, dtype == DA_FP8_E4M3, split, true,
                                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ELAUNCH;
 }

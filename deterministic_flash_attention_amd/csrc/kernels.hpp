@@ -26,6 +26,15 @@ struct PrefillParams {
   int32_t causal;
   float c_scale;      // softmax_scale * q_descale * k_descale * log2(e)
   float v_descale;
+  // Paged K/V (paged extend): k and v are the page caches, keys of sequence b
+  // are its first ctx_lens[b] tokens, token j on page page_table[b][j / 16].
+  const int32_t* page_table;  // [batch, max_pages]
+  const int32_t* ctx_lens;    // [batch]
+  int64_t num_pages;
+  int64_t page_stride;        // elements
+  int64_t token_stride;
+  int64_t head_stride;
+  int32_t max_pages;
 };
 
 struct DecodeParams {
@@ -64,7 +73,7 @@ struct MergeParams {
 };
 
 // Each returns hipSuccess or the launch error.
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, bool split,
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, bool split, bool paged,
                           hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool split,
                          hipStream_t stream);

@@ -32,10 +32,12 @@ namespace detattn {
 
 namespace {
 
-template <int D, bool FP8, int NW>
+template <int D, bool FP8, int NW, bool PAGED = false>
 struct PrefillCfg {
   using G = Geom<D, FP8>;
-  static constexpr bool kDirect = !FP8;  // K/V staged by direct global -> LDS loads
+  // K/V staged by direct global -> LDS loads (contiguous bf16); paged caches
+  // and fp8 go through registers.
+  static constexpr bool kDirect = !FP8 && !PAGED;
   static constexpr int kThreads = NW * kWave;
   static constexpr int kTileRows = 32 * NW;
   static constexpr int kQBytes = kTileRows * G::kQRow;
@@ -75,6 +77,34 @@ struct KVStager {
         const int r = x / G::kChunks16, col = x % G::kChunks16;
         if (kon) kreg[u] = buf_load16(kr, (uint32_t)(kkey0 + r) * row_bytes + (uint32_t)col * 16u);
         if (von) vreg[u] = buf_load16(vr, (uint32_t)(vkey0 + r) * row_bytes + (uint32_t)col * 16u);
+      }
+    }
+  }
+  // Paged caches: key j sits at element offset page_base(j) + (j % 16) *
+  // token_stride, page_base(j) being its page's slot-0 offset for this kv head,
+  // or -1 for a page index outside the cache.  Keys at or past lk and keys on
+  // such pages are staged as zeros, so dead cache slots never reach the MFMA.
+  template <typename PageBase>
+  __device__ __forceinline__ void load_paged(const unsigned char* kc, const unsigned char* vc,
+                                             int key0, int lk, int64_t token_stride,
+                                             const PageBase& page_base, int tid) {
+#pragma unroll
+    for (int u = 0; u < C::kPerThread; ++u) {
+      const int x = tid + u * C::kThreads;
+      if (C::kPerThread * C::kThreads == C::kBlockChunks || x < C::kBlockChunks) {
+        const int r = x / G::kChunks16, col = x % G::kChunks16;
+        const int j = key0 + r;
+        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (j < lk) {
+          const int64_t base = page_base(j);
+          if (base >= 0) {
+            const int64_t byte = (base + (int64_t)(j % 16) * token_stride) * G::kEs + col * 16;
+            kv = *reinterpret_cast<const u32x4*>(kc + byte);
+            vv = *reinterpret_cast<const u32x4*>(vc + byte);
+          }
+        }
+        kreg[u] = kv;
+        vreg[u] = vv;
       }
     }
   }
@@ -161,11 +191,11 @@ struct DirectStager {
   }
 };
 
-template <int D, bool FP8, int NW, int WPE, bool SPLIT>
+template <int D, bool FP8, int NW, int WPE, bool SPLIT, bool PAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void prefill_kernel(const PrefillParams p) {
   using G = Geom<D, FP8>;
-  using C = PrefillCfg<D, FP8, NW>;
+  using C = PrefillCfg<D, FP8, NW, PAGED>;
   static_assert(C::kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
   constexpr int NT = G::kDTiles;
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
@@ -204,8 +234,15 @@ void prefill_kernel(const PrefillParams p) {
 
   const int q_start = uniform(p.cu_q[b]);
   const int lq = uniform(p.cu_q[b + 1]) - q_start;
-  const int k_start = uniform(p.cu_k[b]);
-  const int lk = uniform(p.cu_k[b + 1]) - k_start;
+  // Keys: packed rows [cu_k[b], cu_k[b+1]), or the first ctx_lens[b] tokens of
+  // the sequence's pages (clamped to its page-table row).
+  int k_start = 0, lk;
+  if constexpr (PAGED) {
+    lk = max(0, min(uniform(p.ctx_lens[b]), p.max_pages * 16));
+  } else {
+    k_start = uniform(p.cu_k[b]);
+    lk = uniform(p.cu_k[b + 1]) - k_start;
+  }
   if (lq <= 0 || q_start < 0 || k_start < 0) return;
   const int ntiles = (lq + C::kTileRows - 1) / C::kTileRows;
   const int tile = ntiles - 1 - tile_rev;
@@ -265,8 +302,14 @@ void prefill_kernel(const PrefillParams p) {
                                                  (p.total_q * p.hq - q_head) * G::kRowBytes));
     const uint32_t kv_ext = extent_bytes(lk, kv_row_bytes, G::kRowBytes,
                                          (p.total_k * p.hkv - kv_head) * G::kRowBytes);
-    const rsrc_t kr = make_rsrc(kb, kv_ext);
-    const rsrc_t vr = make_rsrc(vb, kv_ext);
+    const rsrc_t kr = make_rsrc(kb, PAGED ? 0u : kv_ext);
+    const rsrc_t vr = make_rsrc(vb, PAGED ? 0u : kv_ext);
+    // Paged caches: the kv head's slot-0 offset of a page, -1 outside the cache.
+    const int32_t* const table = PAGED ? p.page_table + (int64_t)b * p.max_pages : nullptr;
+    auto page_base = [&](int j) -> int64_t {
+      const int64_t pg = table[j / 16];
+      return (pg >= 0 && pg < p.num_pages) ? pg * p.page_stride + (int64_t)g * p.head_stride : -1;
+    };
 
     if constexpr (C::kDirect && NW == 8) {
     // Ping-pong (bf16 staged directly, two waves per SIMD).  Each wave
@@ -356,11 +399,19 @@ void prefill_kernel(const PrefillParams p) {
     const int wv = uniform(wave);
     DirectStager<D, NW> dst;
     KVStager<D, FP8, NW> rst;
+    auto reg_load = [&](int blk) {
+      if constexpr (PAGED) {
+        rst.load_paged(static_cast<const unsigned char*>(p.k), static_cast<const unsigned char*>(p.v),
+                       blk * kBlockKeys, lk, p.token_stride, page_base, tid);
+      } else {
+        rst.load(kr, blk * kBlockKeys, true, vr, blk * kBlockKeys, true, kv_row_bytes, tid);
+      }
+    };
     if constexpr (C::kDirect) {
       dst.init(wv, lane, kv_row_bytes);
       dst.issue(kr, vr, (uint32_t)(blk_begin * kBlockKeys) * kv_row_bytes, sK, sV, wv);
     } else {
-      rst.load(kr, blk_begin * kBlockKeys, true, vr, blk_begin * kBlockKeys, true, kv_row_bytes, tid);
+      reg_load(blk_begin);
     }
     // Q tile -> LDS (rows past the sequence read as zero).
     for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
@@ -386,8 +437,7 @@ void prefill_kernel(const PrefillParams p) {
           dst.issue(kr, vr, (uint32_t)((blk + 1) * kBlockKeys) * kv_row_bytes,
                     sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, wv);
         } else {
-          rst.load(kr, (blk + 1) * kBlockKeys, true, vr, (blk + 1) * kBlockKeys, true, kv_row_bytes,
-                   tid);
+          reg_load(blk + 1);
         }
       }
       f32x16 s[2];
@@ -480,14 +530,20 @@ void prefill_kernel(const PrefillParams p) {
 }
 
 template <int D, bool FP8, int NW, int WPE>
-hipError_t launch_one(const PrefillParams& p, bool split, hipStream_t stream) {
+hipError_t launch_one(const PrefillParams& p, bool split, bool paged, hipStream_t stream) {
   const long long per = (long long)p.batch * p.hq * p.tiles * (split ? p.cmax : 1);
   if (per <= 0) return hipSuccess;
   dim3 grid((unsigned)per), block(NW * kWave);
-  if (split) {
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, true>), grid, block, 0, stream, p);
+  if (paged) {
+    if (split) {
+      hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, true, true>), grid, block, 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, false, true>), grid, block, 0, stream, p);
+    }
+  } else if (split) {
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, true, false>), grid, block, 0, stream, p);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -503,9 +559,9 @@ struct Layout {
 };
 
 template <int D, bool FP8>
-hipError_t launch_layout(const PrefillParams& p, bool split, hipStream_t stream) {
+hipError_t launch_layout(const PrefillParams& p, bool split, bool paged, hipStream_t stream) {
   using L = Layout<D, FP8>;
-  return launch_one<D, FP8, L::kWaves, L::kWavesPerEU>(p, split, stream);
+  return launch_one<D, FP8, L::kWaves, L::kWavesPerEU>(p, split, paged, stream);
 }
 
 }  // namespace
@@ -519,18 +575,18 @@ int prefill_tile_rows(int head_dim, bool fp8) {
   }
 }
 
-hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, bool split,
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, bool split, bool paged,
                           hipStream_t stream) {
   switch (head_dim) {
     case 64:
-      return fp8 ? launch_layout<64, true>(p, split, stream)
-                 : launch_layout<64, false>(p, split, stream);
+      return fp8 ? launch_layout<64, true>(p, split, paged, stream)
+                 : launch_layout<64, false>(p, split, paged, stream);
     case 128:
-      return fp8 ? launch_layout<128, true>(p, split, stream)
-                 : launch_layout<128, false>(p, split, stream);
+      return fp8 ? launch_layout<128, true>(p, split, paged, stream)
+                 : launch_layout<128, false>(p, split, paged, stream);
     case 192:
-      return fp8 ? launch_layout<192, true>(p, split, stream)
-                 : launch_layout<192, false>(p, split, stream);
+      return fp8 ? launch_layout<192, true>(p, split, paged, stream)
+                 : launch_layout<192, false>(p, split, paged, stream);
     default:
       return hipErrorInvalidValue;
   }

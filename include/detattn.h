@@ -145,6 +145,35 @@ da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cach
                                 void* o, float* lse, void* stream);
 
 /*
+ * Prefix-cached extend over a paged KV cache, for a batch that mixes prefill,
+ * extend and decode sequences in one launch (RL-Kernel page, section 2: the
+ * same arithmetic path serves prefill, prefix-cached extend and paged decode).
+ * Sequence b has L_k = context_lens[b] cached tokens (its prefix and its new
+ * tokens, already written to the cache) and L_q = cu_seqlens_q[b+1] -
+ * cu_seqlens_q[b] query rows, which are its last L_q tokens: L_q = L_k is a
+ * prefill, L_q < L_k an extend, L_q = 1 a decode step.  With causal == 1 row i
+ * sees keys j <= i + L_k - L_q (bottom-right); with causal == 0 every cached key.
+ *   q, cu_seqlens_q, total_q, max_seqlen_q  as for attn_prefill_fwd.
+ *   k_cache, v_cache, num_pages, the strides, page_table, max_pages_per_seq,
+ *   context_lens, max_context_len, page_size  as for attn_decode_split_fwd
+ *            (no limit on Hq / Hkv here).
+ *   schedule  as for attn_prefill_fwd, with max_chunks = attn_num_chunks(max_context_len).
+ * Each row is bitwise equal to the same row computed by attn_prefill_fwd over
+ * the gathered keys, and a decode row to attn_decode_split_fwd's, whichever
+ * sequences share the launch.
+ */
+da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_seqlens_q,
+                                const void* k_cache, const void* v_cache, int64_t num_pages,
+                                int64_t page_stride, int64_t token_stride, int64_t head_stride,
+                                const int32_t* page_table, int32_t max_pages_per_seq,
+                                const int32_t* context_lens, int32_t batch, int32_t max_seqlen_q,
+                                int32_t max_context_len, int64_t total_q, int32_t page_size,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                float softmax_scale, int32_t causal, float q_descale,
+                                float k_descale, float v_descale, int32_t schedule, void* o,
+                                float* lse, float* partials, size_t partials_bytes, void* stream);
+
+/*
  * Fold chunk partials into O: for every (row, head), partials c = 0 .. max_chunks-1
  * are merged left to right with the exact max/sum rescale (empty partials,
  * m = -inf, are skipped), then O = A / L (0 when L = 0) times v_descale is

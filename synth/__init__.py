@@ -34,6 +34,13 @@ CAUSAL_VARLEN = dict(name="causal_gqa_varlen", seqlens=[4096, 2500, 1, 3969], hq
 PAGED_DECODE = dict(name="paged_decode", batch=64, hq=32, hkv=8, d=128, page_size=16,
                     ctx_min=1, ctx_max=32768, spare_pages=1024)
 FP8_WIDE = dict(name="fp8_wide_head", seqlens=[8192], hq=32, hkv=32, d=192)
+# One launch over a paged cache mixing the causal varlen prefill sequences,
+# 512-token extends of prefixes that cross chunk boundaries, and decode steps
+# (one query token) at short to maximal contexts; GQA 32/8, D=128.
+MIXED_EXTEND = dict(name="mixed_paged_extend", hq=32, hkv=8, d=128, page_size=16, spare_pages=64,
+                    ctx_lens=[4096, 2500, 3969, 8704, 8704, 16896, 16896, 1000, 9000, 20000,
+                              32768],
+                    q_lens=[4096, 2500, 3969, 512, 512, 512, 512, 1, 1, 1, 1])
 
 
 def _gen(seed: int) -> torch.Generator:
@@ -198,6 +205,102 @@ def decode_inputs(seed: int, batch: int, hq: int, hkv: int, d: int, page_size: i
         return DecodeInputs(qf.codes, kc, vc, table, ctx.to(torch.int32), hq, hkv, d, page_size,
                             float(scale), seed, "fp8", qf.scale, kf.scale, vf.scale)
     raise ValueError(dtype)
+
+
+@dataclasses.dataclass
+class ExtendInputs:
+    """A mixed prefill / extend / decode batch over a paged KV cache.
+
+    Sequence b has ctx_lens[b] tokens and q_lens[b] query rows, its last
+    q_lens[b] tokens.  ``q_full``/``k``/``v`` hold every token of every sequence
+    packed contiguously (``cu_full``), ``q`` the query rows only (``cu_seqlens_q``),
+    and the caches the same K/V tokens placed in pages by a seeded random table."""
+    q: torch.Tensor             # [sum(q_lens), Hq, D]
+    cu_seqlens_q: torch.Tensor  # int32 [B+1]
+    q_full: Optional[torch.Tensor]  # [sum(ctx_lens), Hq, D] (with full_q) or None
+    k: torch.Tensor             # [sum(ctx_lens), Hkv, D]
+    v: torch.Tensor
+    cu_full: torch.Tensor       # int32 [B+1] over ctx_lens
+    k_cache: torch.Tensor       # [num_pages, page_size, Hkv, D]
+    v_cache: torch.Tensor
+    page_table: torch.Tensor    # int32 [B, max_pages]
+    context_lens: torch.Tensor  # int32 [B]
+    q_lens: list
+    ctx_lens: list
+    hq: int
+    hkv: int
+    d: int
+    page_size: int
+    scale: float
+    causal: bool
+    dtype: str = "bf16"
+    q_scale: float = 1.0
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+    seed: int = 0
+
+
+def extend_inputs(seed: int, ctx_lens: Sequence[int], q_lens: Sequence[int], hq: int, hkv: int,
+                  d: int, causal: bool = True, page_size: int = 16, spare_pages: int = 8,
+                  poison: bool = True, dtype: str = "bf16", scale: Optional[float] = None,
+                  full_q: bool = False) -> ExtendInputs:
+    """K/V ~ N(0,1) for every token, Q ~ N(0,1) for the query rows of each
+    sequence's tail (for every token with ``full_q``), and a paged copy of K/V
+    (dead slots and spare pages NaN when ``poison``)."""
+    ctx_lens = [int(x) for x in ctx_lens]
+    q_lens = [int(x) for x in q_lens]
+    assert len(ctx_lens) == len(q_lens) and all(0 <= a <= b for a, b in zip(q_lens, ctx_lens))
+    g = _gen(seed)
+    tk = sum(ctx_lens)
+    if scale is None:
+        scale = 1.0 / float(np.sqrt(d))
+    q32 = torch.randn(tk if full_q else sum(q_lens), hq, d, generator=g)
+    k32 = torch.randn(tk, hkv, d, generator=g)
+    v32 = torch.randn(tk, hkv, d, generator=g)
+    pages = [(c + page_size - 1) // page_size for c in ctx_lens]
+    num_pages = sum(pages) + spare_pages
+    max_pages = max(1, max(pages) if pages else 1)
+    perm = torch.randperm(num_pages, generator=g)
+    table = torch.zeros(len(ctx_lens), max_pages, dtype=torch.int32)
+    pos = 0
+    for b, n in enumerate(pages):
+        table[b, :n] = perm[pos:pos + n].to(torch.int32)
+        pos += n
+        if n < max_pages:  # unused entries point at spare pages (or page 0)
+            spare = perm[sum(pages):] if spare_pages > 0 else torch.zeros(1, dtype=torch.int64)
+            table[b, n:] = spare[torch.arange(max_pages - n) % len(spare)].to(torch.int32)
+    if dtype == "bf16":
+        qf, kf, vf = q32.to(torch.bfloat16), k32.to(torch.bfloat16), v32.to(torch.bfloat16)
+        qs = ks = vs = 1.0
+        dead = torch.tensor(float("nan")).to(torch.bfloat16)
+        zero_cache = torch.zeros(num_pages, page_size, hkv, d, dtype=torch.bfloat16)
+    elif dtype == "fp8":
+        fq, fk, fv = quantize_e4m3(q32), quantize_e4m3(k32), quantize_e4m3(v32)
+        qf, kf, vf = fq.codes, fk.codes, fv.codes
+        qs, ks, vs = fq.scale, fk.scale, fv.scale
+        dead = torch.tensor(0x7F, dtype=torch.uint8)  # E4M3FN NaN code
+        zero_cache = torch.zeros(num_pages, page_size, hkv, d, dtype=torch.uint8)
+    else:
+        raise ValueError(dtype)
+    kc, vc = zero_cache.clone(), zero_cache.clone()
+    if poison:
+        kc[:] = dead
+        vc[:] = dead
+    cu = cu_seqlens(ctx_lens)
+    rows = []
+    for b, c in enumerate(ctx_lens):
+        s0 = int(cu[b])
+        j = torch.arange(c)
+        pg = table[b, (j // page_size)].long()
+        kc[pg, j % page_size] = kf[s0:s0 + c]
+        vc[pg, j % page_size] = vf[s0:s0 + c]
+        rows.append(torch.arange(s0 + c - q_lens[b], s0 + c))
+    idx = torch.cat(rows) if rows else torch.zeros(0, dtype=torch.int64)
+    q_rows = qf[idx].contiguous() if full_q else qf
+    return ExtendInputs(q_rows, cu_seqlens(q_lens), qf if full_q else None, kf, vf, cu, kc, vc,
+                        table,
+                        torch.tensor(ctx_lens, dtype=torch.int32), q_lens, ctx_lens, hq, hkv, d,
+                        page_size, float(scale), bool(causal), dtype, qs, ks, vs, seed)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

@@ -59,6 +59,45 @@ def run_decode(inp: synth.DecodeInputs, schedule: int, return_lse: bool = False,
     return res
 
 
+def run_extend(inp: synth.ExtendInputs, schedule: int, return_lse: bool = False, out=None):
+    """The mixed batch through attn_paged_extend_fwd (plus the merge for SPLIT)."""
+    import deterministic_flash_attention_amd as dfa
+    res = dfa.paged_extend(dev(inp.q), dev(inp.cu_seqlens_q), dev(inp.k_cache), dev(inp.v_cache),
+                           dev(inp.page_table), dev(inp.context_lens), max(inp.q_lens),
+                           max(inp.ctx_lens), inp.causal, softmax_scale=inp.scale,
+                           schedule=schedule, descales=descales(inp), out=out,
+                           return_lse=return_lse)
+    torch.cuda.synchronize()
+    return res
+
+
+def oracle_extend(inp: synth.ExtendInputs, rows=None):
+    """fp64 oracle of a paged extend batch: each sequence's keys gathered from
+    its pages by the oracle (over the sequence's own pages, widened to fp64),
+    then the packed-varlen definition with bottom-right alignment."""
+    ps = inp.page_size
+
+    ks, vs = [], []
+    for b, c in enumerate(inp.ctx_lens):
+        pages = inp.page_table[b, :(c + ps - 1) // ps].long()
+        local = np.arange(len(pages))
+        kp, vp = inp.k_cache[pages], inp.v_cache[pages]
+        if inp.dtype == "fp8":
+            kp = oracle.dequantize_e4m3(kp.numpy(), inp.k_scale)
+            vp = oracle.dequantize_e4m3(vp.numpy(), inp.v_scale)
+        else:
+            kp, vp = synth.to_f64(kp), synth.to_f64(vp)
+        ks.append(oracle.gather_pages(kp, local, c, ps))
+        vs.append(oracle.gather_pages(vp, local, c, ps))
+    if inp.dtype == "fp8":
+        q = oracle.dequantize_e4m3(inp.q.numpy(), inp.q_scale)
+    else:
+        q = synth.to_f64(inp.q)
+    return oracle.attention(q, np.concatenate(ks), np.concatenate(vs), inp.cu_seqlens_q.numpy(),
+                            inp.cu_full.numpy(), inp.hq, inp.hkv, inp.scale, inp.causal,
+                            rows=rows)
+
+
 def compare(gpu_o: torch.Tensor, ref: np.ndarray, fp8: bool, rows=None, label: str = ""):
     """Element-wise comparison against the oracle at the stated tolerance.
 

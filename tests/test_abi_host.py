@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     assert names == sorted(["attn_status_str", "attn_num_chunks", "attn_partials_bytes",
-                            "attn_prefill_fwd", "attn_decode_split_fwd", "attn_chunk_merge"])
+                            "attn_prefill_fwd", "attn_decode_split_fwd",
+                            "attn_paged_extend_fwd", "attn_chunk_merge"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -115,6 +116,43 @@ def _decode_args(**over):
 ])
 def test_decode_validation(lib, over, status):
     assert lib.attn_decode_split_fwd(*_decode_args(**over)) == status
+
+
+def _extend_args(**over):
+    a = dict(dtype=0, q=FAKE, cu_q=FAKE, kc=FAKE, vc=FAKE, num_pages=100,
+             page_stride=16 * 8 * 128, token_stride=8 * 128, head_stride=128, table=FAKE,
+             max_pages=64, ctx=FAKE, batch=4, max_q=300, max_ctx=1024, total_q=600,
+             page_size=16, hq=32, hkv=8, d=128, scale=0.088, causal=1, qd=1.0, kd=1.0, vd=1.0,
+             schedule=0, o=FAKE, lse=None, part=None, part_bytes=0, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=3), DA_EINVAL),
+    (dict(schedule=2), DA_EINVAL),
+    (dict(causal=-1), DA_EINVAL),
+    (dict(page_size=8), DA_EUNSUPPORTED),
+    (dict(d=256), DA_EUNSUPPORTED),
+    (dict(hq=30, hkv=8), DA_EINVAL),
+    (dict(max_ctx=64 * 16 + 1), DA_EINVAL),   # context beyond the page table
+    (dict(num_pages=0), DA_EINVAL),
+    (dict(page_stride=-5), DA_EINVAL),
+    (dict(token_stride=4), DA_EINVAL),        # 8-byte stride is not a multiple of 16
+    (dict(cu_q=None), DA_EINVAL),
+    (dict(table=None), DA_EINVAL),
+    (dict(ctx=None), DA_EINVAL),
+    (dict(kc=FAKE + 4), DA_EINVAL),           # misaligned cache
+    (dict(o=None), DA_EINVAL),
+    (dict(scale=float("inf")), DA_EINVAL),
+    (dict(kd=3.0), DA_EINVAL),                # descales must be 1 for bf16
+    (dict(schedule=1, part=None), DA_EINVAL),
+    (dict(schedule=1, part=FAKE, part_bytes=4096), DA_EWORKSPACE),
+    (dict(max_q=1 << 28), DA_EUNSUPPORTED),   # beyond 32-bit descriptor offsets
+    (dict(batch=0), DA_OK),                   # no work: nothing launched
+])
+def test_paged_extend_validation(lib, over, status):
+    assert lib.attn_paged_extend_fwd(*_extend_args(**over)) == status
 
 
 @pytest.mark.parametrize("args,status", [
