@@ -152,6 +152,10 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
       !aligned(v_cache, 16) || !aligned(page_table, 4) || !aligned(context_lens, 4))
     return DA_EINVAL;
   if ((page_stride * es) % 16 || (token_stride * es) % 16 || (head_stride * es) % 16) return DA_EINVAL;
+  // A token's head row must not overlap the next token's; a page's tokens are
+  // addressed with 32-bit offsets.
+  if (token_stride < head_dim) return DA_EINVAL;
+  if (token_stride * es * DA_PAGE_SIZE > kMaxOffset) return DA_EUNSUPPORTED;
   if (!split && (!o || !aligned(o, 16) || (lse && !aligned(lse, 4)))) return DA_EINVAL;
   if (split && (!partials || !aligned(partials, 16))) return DA_EINVAL;
 

@@ -65,10 +65,6 @@ struct Geom {
   static constexpr int kChunks16 = kRowBytes / 16;  // 16-byte chunks per HBM row
 };
 
-// Q^T operand of one K-step: 8 bf16 (16 bytes) or 8 e4m3 (8 bytes) per lane.
-template <bool FP8> struct QFrag { u32x4 v; };
-template <> struct QFrag<true> { u32x2 v; };
-
 // Score element i of key tile t in lane (n, h = lane/32) is the key at offset
 // 32t + 16(i/8) + 8h + (i%8) of the block: MFMA row r of tile t holds key
 // 32t + sigma(r), sigma swapping bits 2 and 3 of r, so that each lane holds 8
@@ -82,38 +78,17 @@ __device__ __forceinline__ int score_key(int t, int i, int h) {
 }
 
 // S^T = K_blk Q^T for the 64 keys of the staged block; s[t] holds key tile t.
-template <int D, bool FP8>
-__device__ __forceinline__ void qk_scores(f32x16 (&s)[2], const QFrag<FP8> (&q)[D / 16],
-                                          const unsigned char* ks, int lane) {
-  using G = Geom<D, FP8>;
-  const int row = key_sigma(lane & 31);
-  const int h = lane >> 5;
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
-#pragma unroll
-  for (int st = 0; st < G::kSteps; ++st) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t off = (uint32_t)((32 * t + row) * G::kKRow + (16 * st + 8 * h) * G::kEs);
-      if constexpr (FP8) {
-        s[t] = mfma_fp8(lds_load8(ks, off), q[st].v, s[t]);
-      } else {
-        s[t] = mfma_bf16(lds_load16(ks, off), q[st].v, s[t]);
-      }
-    }
-  }
-}
-
-// Same product with the lane's Q^T operands read from LDS: qrow points at the
-// lane's query row (row stride irrelevant; D elements of Q).
-template <int D, bool FP8>
+// qrow points at the lane's query row in LDS (D elements of Q).  K rows sit in
+// groups of 16 (one cache page) KPAGE bytes apart, G::kKRow apart inside a
+// group; KPAGE = 16 * kKRow is the plain row-major stage.
+template <int D, bool FP8, int KPAGE = 16 * Geom<D, FP8>::kKRow>
 __device__ __forceinline__ void qk_scores_qrow(f32x16 (&s)[2], const unsigned char* qrow,
                                                const unsigned char* ks, int lane) {
   using G = Geom<D, FP8>;
+  static_assert(KPAGE >= 16 * G::kKRow, "a page group holds 16 K rows");
   const int row = key_sigma(lane & 31);
   const int h = lane >> 5;
+  const int krow = (row >> 4) * KPAGE + (row & 15) * G::kKRow;  // key tile 0; tile 1 is 2 groups on
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -123,7 +98,7 @@ __device__ __forceinline__ void qk_scores_qrow(f32x16 (&s)[2], const unsigned ch
     const uint32_t qoff = (uint32_t)((16 * st + 8 * h) * G::kEs);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint32_t off = (uint32_t)((32 * t + row) * G::kKRow + (16 * st + 8 * h) * G::kEs);
+      const uint32_t off = (uint32_t)(krow + 2 * t * KPAGE + (16 * st + 8 * h) * G::kEs);
       if constexpr (FP8) {
         s[t] = mfma_fp8(lds_load8(ks, off), lds_load8(qrow, qoff), s[t]);
       } else {
@@ -135,10 +110,10 @@ __device__ __forceinline__ void qk_scores_qrow(f32x16 (&s)[2], const unsigned ch
 
 // Same product with the Q^T operands read from the wave's rows of the LDS Q tile
 // (qs points at the wave's first row; row stride G::kQRow).
-template <int D, bool FP8>
+template <int D, bool FP8, int KPAGE = 16 * Geom<D, FP8>::kKRow>
 __device__ __forceinline__ void qk_scores_qlds(f32x16 (&s)[2], const unsigned char* qs,
                                                const unsigned char* ks, int lane) {
-  qk_scores_qrow<D, FP8>(s, qs + (lane & 31) * Geom<D, FP8>::kQRow, ks, lane);
+  qk_scores_qrow<D, FP8, KPAGE>(s, qs + (lane & 31) * Geom<D, FP8>::kQRow, ks, lane);
 }
 
 // Combine a value with the one in lane ^ 32.  v_permlane32_swap exchanges the

@@ -35,19 +35,27 @@ namespace {
 template <int D, bool FP8, int NW, bool PAGED = false>
 struct PrefillCfg {
   using G = Geom<D, FP8>;
-  // K/V staged by direct global -> LDS loads (contiguous bf16); paged caches
-  // and fp8 go through registers.
-  static constexpr bool kDirect = !FP8 && !PAGED;
+  // K/V staged by direct global -> LDS loads for bf16 (paged: up to D = 128,
+  // where the page-aligned stages fit); otherwise through registers (fp8 V is
+  // widened on the way).
+  static constexpr bool kDirect = !FP8 && (!PAGED || D <= 128);
   static constexpr int kThreads = NW * kWave;
   static constexpr int kTileRows = 32 * NW;
   static constexpr int kQBytes = kTileRows * G::kQRow;
   static constexpr int kBlockChunks = kBlockKeys * G::kChunks16;  // 16-B chunks per K block
   static constexpr int kPerThread = (kBlockChunks + kThreads - 1) / kThreads;
+  // K rows in groups of 16 (one cache page); a directly staged paged K stage
+  // pads each group to whole 1 KB segments so that no segment spans two pages.
+  static constexpr int kKPage =
+      (PAGED && kDirect) ? (16 * G::kKRow + 1023) / 1024 * 1024 : 16 * G::kKRow;
+  static constexpr int kKStage = 4 * kKPage;
+  static constexpr int kVStage = G::kVStage;  // 16 V rows are whole 1 KB segments
   static constexpr int kKOff = kQBytes;
-  static constexpr int kVOff = kKOff + 2 * G::kKStage;
-  static constexpr int kLds = kVOff + 2 * G::kVStage;
+  static constexpr int kVOff = kKOff + 2 * kKStage;
+  static constexpr int kLds = kVOff + 2 * kVStage;
   // Q tile, the two K stages and the two V stages are disjoint byte ranges.
-  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * G::kKStage, "LDS regions overlap");
+  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * kKStage, "LDS regions overlap");
+  static_assert(kDirect || kKPage == 16 * G::kKRow, "register staging writes row-major stages");
 };
 
 __device__ __forceinline__ uint32_t extent_bytes(int64_t nrows, int64_t row_bytes,
@@ -131,11 +139,12 @@ struct KVStager {
   }
 };
 
-// Direct staging of one bf16 K block and one V block into their padded stages.
-// A stage is a whole number of 1 KB segments; one wave instruction fills one
-// segment, lane i the 16-byte slot i of it.  A slot is a 16-byte chunk of a
-// K/V row or a row's padding; padding lanes load from a parked offset, which
-// the range check turns into zeros.  Rows past the sequence read as zeros.
+// Direct staging of bf16 K and V blocks of a packed sequence into their padded
+// stages.  A stage is a whole number of 1 KB segments; one wave instruction
+// fills one segment, lane i the 16-byte slot i of it.  A slot is a 16-byte
+// chunk of a K/V row or a row's padding; padding lanes load from a parked
+// offset, which the range check turns into zeros.  Rows past the sequence
+// read as zeros (the descriptors end at its last key row).
 template <int D, int NW>
 struct DirectStager {
   using G = Geom<D, false>;
@@ -148,45 +157,135 @@ struct DirectStager {
                 "a stage must be whole 1 KB segments");
   uint32_t koff[kKPer];  // this lane's byte offset inside a block, per segment of this wave
   uint32_t voff[kVPer];
+  rsrc_t kr, vr;
+  uint32_t row_bytes;
 
   static __device__ __forceinline__ uint32_t slot_offset(int seg, int lane, int slots,
                                                          uint32_t row_bytes) {
     const int s = 64 * seg + lane, row = s / slots, c = s % slots;
     return c < G::kChunks16 ? (uint32_t)row * row_bytes + 16u * (uint32_t)c : kParked;
   }
-  __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes) {
+  __device__ __forceinline__ void init(int wave, int lane, rsrc_t k, rsrc_t v, uint32_t rb) {
+    kr = k;
+    vr = v;
+    row_bytes = rb;
 #pragma unroll
-    for (int u = 0; u < kKPer; ++u) koff[u] = slot_offset(wave + u * NW, lane, kKSlots, row_bytes);
+    for (int u = 0; u < kKPer; ++u) koff[u] = slot_offset(wave + u * NW, lane, kKSlots, rb);
 #pragma unroll
-    for (int u = 0; u < kVPer; ++u) voff[u] = slot_offset(wave + u * NW, lane, kVSlots, row_bytes);
+    for (int u = 0; u < kVPer; ++u) voff[u] = slot_offset(wave + u * NW, lane, kVSlots, rb);
   }
-  // blk_off = first key of the block times the row stride (below 2^31, so a
-  // parked offset plus it stays out of range without wrapping).
-  __device__ __forceinline__ void issue_k(rsrc_t kr, uint32_t blk_off, unsigned char* ks, int wave) const {
+  __device__ __forceinline__ void prefetch(int, int) {}  // nothing to look up
+  // The block offset (first key times the row stride) is below 2^31, so a
+  // parked offset plus it stays out of range without wrapping.
+  __device__ __forceinline__ void issue_k(int blk, unsigned char* ks, int wave) const {
+    const uint32_t blk_off = (uint32_t)(blk * kBlockKeys) * row_bytes;
 #pragma unroll
     for (int u = 0; u < kKPer; ++u) {
       const int seg = wave + u * NW;
       if (kKPer * NW == kKSlots || seg < kKSlots) buf_load16_lds(kr, ks + seg * 1024, koff[u] + blk_off);
     }
   }
-  __device__ __forceinline__ void issue_v(rsrc_t vr, uint32_t blk_off, unsigned char* vs, int wave) const {
+  __device__ __forceinline__ void issue_v(int blk, unsigned char* vs, int wave) const {
+    const uint32_t blk_off = (uint32_t)(blk * kBlockKeys) * row_bytes;
 #pragma unroll
     for (int u = 0; u < kVPer; ++u) {
       const int seg = wave + u * NW;
       if (kVPer * NW == kVSlots || seg < kVSlots) buf_load16_lds(vr, vs + seg * 1024, voff[u] + blk_off);
     }
   }
-  __device__ __forceinline__ void issue(rsrc_t kr, rsrc_t vr, uint32_t blk_off, unsigned char* ks,
-                                        unsigned char* vs, int wave) const {
+};
+
+// Direct staging of bf16 K and V blocks from a paged cache.  A block is four
+// 16-token pages; each stage holds them as four page regions of whole 1 KB
+// segments (K rows padded to KPAGE per region, V regions exactly 16 rows), so
+// every segment comes from one page.  NW/4 waves share a page region, so each
+// wave reads one page per operand and block, through a descriptor based at
+// the page's slot 0 for this kv head whose num_records ends at the page's last
+// live token.  Slots past it, padding slots and pages whose table entry lies
+// outside the cache (a descriptor of zero records) read as zeros.
+template <int D, int NW, int KPAGE>
+struct PagedDirectStager {
+  using G = Geom<D, false>;
+  static constexpr int kWavesPerPage = NW / 4;
+  static constexpr int kKSegs = KPAGE / 1024;          // segments per page region
+  static constexpr int kVSegs = 16 * G::kVRow / 1024;
+  static constexpr int kKSlots = G::kKRow / 16;        // slots per padded row
+  static constexpr int kVSlots = G::kVRow / 16;
+  static constexpr int kKPer = (kKSegs + kWavesPerPage - 1) / kWavesPerPage;  // per wave
+  static constexpr int kVPer = (kVSegs + kWavesPerPage - 1) / kWavesPerPage;
+  static_assert(NW % 4 == 0, "waves are dealt evenly to the four pages of a block");
+  static_assert(KPAGE % 1024 == 0 && (16 * G::kVRow) % 1024 == 0 && KPAGE >= 16 * G::kKRow,
+                "page regions must be whole 1 KB segments holding 16 rows");
+  uint32_t koff[kKPer];  // this lane's byte offset inside the page, per segment of this wave
+  uint32_t voff[kVPer];
+  const unsigned char* kc;  // caches at this kv head's offset
+  const unsigned char* vc;
+  const int32_t* table;     // this sequence's page-table row
+  int64_t num_pages;
+  int64_t page_bytes;
+  uint32_t token_bytes;
+  int lk;
+  int max_pages;
+  int page;                 // this wave's page of every block (0..3)
+  int sub;                  // and its rank among the waves of that page
+  int32_t kent, vent;       // table entries of this wave's pages of the next K and V blocks
+
+  static __device__ __forceinline__ uint32_t slot_offset(int sp, int lane, int slots,
+                                                         uint32_t token_bytes) {
+    const int s = 64 * sp + lane, row = s / slots, c = s % slots;
+    return (row < 16 && c < G::kChunks16) ? (uint32_t)row * token_bytes + 16u * (uint32_t)c
+                                          : kParked;
+  }
+  __device__ __forceinline__ void init(int wave, int lane, const unsigned char* k,
+                                       const unsigned char* v, const int32_t* tab, int64_t npages,
+                                       int64_t pbytes, uint32_t tbytes, int keys, int mpages) {
+    kc = k;
+    vc = v;
+    table = tab;
+    num_pages = npages;
+    page_bytes = pbytes;
+    token_bytes = tbytes;
+    lk = keys;
+    max_pages = mpages;
+    page = wave / kWavesPerPage;
+    sub = wave % kWavesPerPage;
+#pragma unroll
+    for (int u = 0; u < kKPer; ++u) koff[u] = slot_offset(sub + u * kWavesPerPage, lane, kKSlots, tbytes);
+#pragma unroll
+    for (int u = 0; u < kVPer; ++u) voff[u] = slot_offset(sub + u * kWavesPerPage, lane, kVSlots, tbytes);
+  }
+  // Read this wave's table entries of K block kblk and V block vblk, to be
+  // issued next; indices are clamped into the table row (entries of pages
+  // without a live token are never used).
+  __device__ __forceinline__ void prefetch(int kblk, int vblk) {
+    kent = table[max(0, min(kblk * 4 + page, max_pages - 1))];
+    vent = table[max(0, min(vblk * 4 + page, max_pages - 1))];
+  }
+  // Descriptor of this wave's page of block blk, whose table entry is pg.
+  __device__ __forceinline__ rsrc_t page_rsrc(const unsigned char* cache, int blk,
+                                              int32_t pg) const {
+    const int live = min(16, lk - (blk * kBlockKeys + 16 * page));
+    const bool ok = live > 0 && pg >= 0 && (int64_t)pg < num_pages;
+    return make_rsrc(cache + (ok ? (int64_t)pg * page_bytes : 0),
+                     ok ? (uint32_t)(live - 1) * token_bytes + (uint32_t)G::kRowBytes : 0u);
+  }
+  // Issue K block blk / V block blk: the last prefetch must have named it.
+  __device__ __forceinline__ void issue_k(int blk, unsigned char* ks, int) const {
+    const rsrc_t r = page_rsrc(kc, blk, kent);
+    unsigned char* const base = ks + page * KPAGE;
 #pragma unroll
     for (int u = 0; u < kKPer; ++u) {
-      const int seg = wave + u * NW;
-      if (kKPer * NW == kKSlots || seg < kKSlots) buf_load16_lds(kr, ks + seg * 1024, koff[u] + blk_off);
+      const int sp = sub + u * kWavesPerPage;
+      if (kKPer * kWavesPerPage == kKSegs || sp < kKSegs) buf_load16_lds(r, base + sp * 1024, koff[u]);
     }
+  }
+  __device__ __forceinline__ void issue_v(int blk, unsigned char* vs, int) const {
+    const rsrc_t r = page_rsrc(vc, blk, vent);
+    unsigned char* const base = vs + page * (16 * G::kVRow);
 #pragma unroll
     for (int u = 0; u < kVPer; ++u) {
-      const int seg = wave + u * NW;
-      if (kVPer * NW == kVSlots || seg < kVSlots) buf_load16_lds(vr, vs + seg * 1024, voff[u] + blk_off);
+      const int sp = sub + u * kWavesPerPage;
+      if (kVPer * kWavesPerPage == kVSegs || sp < kVSegs) buf_load16_lds(r, base + sp * 1024, voff[u]);
     }
   }
 };
@@ -310,6 +409,24 @@ void prefill_kernel(const PrefillParams p) {
       const int64_t pg = table[j / 16];
       return (pg >= 0 && pg < p.num_pages) ? pg * p.page_stride + (int64_t)g * p.head_stride : -1;
     };
+    const int wv = uniform(wave);
+    // The direct stager of this sequence's keys (packed rows or cache pages).
+    auto make_direct = [&]() {
+      if constexpr (!C::kDirect) {
+        return 0;  // staged through registers
+      } else if constexpr (PAGED) {
+        PagedDirectStager<D, NW, C::kKPage> st;
+        const int64_t head_off = (int64_t)g * p.head_stride * G::kEs;
+        st.init(wv, lane, static_cast<const unsigned char*>(p.k) + head_off,
+                static_cast<const unsigned char*>(p.v) + head_off, table, p.num_pages,
+                p.page_stride * G::kEs, (uint32_t)(p.token_stride * G::kEs), lk, p.max_pages);
+        return st;
+      } else {
+        DirectStager<D, NW> st;
+        st.init(wv, lane, kr, vr, kv_row_bytes);
+        return st;
+      }
+    };
 
     if constexpr (C::kDirect && NW == 8) {
     // Ping-pong (bf16 staged directly, two waves per SIMD).  Each wave
@@ -331,15 +448,16 @@ void prefill_kernel(const PrefillParams p) {
     // in 2j, 2j+1: every write falls after the last read of the block two
     // earlier in the same stage and before the first read of its own block.
     const int n = blk_end - blk_begin;
-    const int wv = uniform(wave);
     const int lag = wv >= NW / 2 ? 1 : 0;
-    DirectStager<D, NW> dst;
-    dst.init(wv, lane, kv_row_bytes);
-    auto key_off = [&](int blk) { return (uint32_t)(blk * kBlockKeys) * kv_row_bytes; };
-    // event e: K block e+1 -> K stage (e+1)&1, V block e -> V stage e&1 (relative blocks)
+    auto dst = make_direct();
+    // event e: K block e+1 -> K stage (e+1)&1, V block e -> V stage e&1 (relative
+    // blocks).  A wave's events run in order, so after issuing event e it looks
+    // up (paged caches) the blocks of event e+1.
+    dst.prefetch(blk_begin, blk_begin - 1);
     auto event = [&](int e) {
-      if (e + 1 < n) dst.issue_k(kr, key_off(blk_begin + e + 1), sK + ((e + 1) & 1) * G::kKStage, wv);
-      if (e >= 0 && e < n) dst.issue_v(vr, key_off(blk_begin + e), sV + (e & 1) * G::kVStage, wv);
+      if (e + 1 < n) dst.issue_k(blk_begin + e + 1, sK + ((e + 1) & 1) * C::kKStage, wv);
+      if (e >= 0 && e < n) dst.issue_v(blk_begin + e, sV + (e & 1) * C::kVStage, wv);
+      dst.prefetch(blk_begin + e + 2, blk_begin + e + 1);
     };
     event(-1);
     if (lag) event(0);
@@ -371,13 +489,13 @@ void prefill_kernel(const PrefillParams p) {
       const int blk = blk_begin + j;
       __builtin_amdgcn_s_setprio(2);  // MFMA phase ahead of the other half's VALU
       if (j > 0) {
-        pv_mfma<D, NT>(acc, 0, pb, sV + ((j - 1) & 1) * G::kVStage, lane);
+        pv_mfma<D, NT>(acc, 0, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
         if constexpr (!SPLIT) {
           if (blk % kBlocksPerChunk == 0) fold_chunk();
         }
       }
       f32x16 s[2];
-      qk_scores_qlds<D, FP8>(s, sQw, sK + (j & 1) * G::kKStage, lane);
+      qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + (j & 1) * C::kKStage, lane);
       __syncthreads();
       __builtin_amdgcn_s_setprio(0);
       event(j + lag);
@@ -391,13 +509,11 @@ void prefill_kernel(const PrefillParams p) {
       wait_vm();
       __syncthreads();
     }
-    pv_mfma<D, NT>(acc, 0, pb, sV + ((n - 1) & 1) * G::kVStage, lane);
+    pv_mfma<D, NT>(acc, 0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
     if constexpr (!SPLIT) fold_chunk();
     if (!lag) __syncthreads();
       } else {
     const int n = blk_end - blk_begin;
-    const int wv = uniform(wave);
-    DirectStager<D, NW> dst;
     KVStager<D, FP8, NW> rst;
     auto reg_load = [&](int blk) {
       if constexpr (PAGED) {
@@ -407,9 +523,11 @@ void prefill_kernel(const PrefillParams p) {
         rst.load(kr, blk * kBlockKeys, true, vr, blk * kBlockKeys, true, kv_row_bytes, tid);
       }
     };
+    auto dst = make_direct();
     if constexpr (C::kDirect) {
-      dst.init(wv, lane, kv_row_bytes);
-      dst.issue(kr, vr, (uint32_t)(blk_begin * kBlockKeys) * kv_row_bytes, sK, sV, wv);
+      dst.prefetch(blk_begin, blk_begin);
+      dst.issue_k(blk_begin, sK, wv);
+      dst.issue_v(blk_begin, sV, wv);
     } else {
       reg_load(blk_begin);
     }
@@ -434,14 +552,15 @@ void prefill_kernel(const PrefillParams p) {
       // barrier that ended block j-1.
       if (more) {
         if constexpr (C::kDirect) {
-          dst.issue(kr, vr, (uint32_t)((blk + 1) * kBlockKeys) * kv_row_bytes,
-                    sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, wv);
+          dst.prefetch(blk + 1, blk + 1);
+          dst.issue_k(blk + 1, sK + (cur ^ 1) * C::kKStage, wv);
+          dst.issue_v(blk + 1, sV + (cur ^ 1) * C::kVStage, wv);
         } else {
           reg_load(blk + 1);
         }
       }
       f32x16 s[2];
-      qk_scores_qlds<D, FP8>(s, sQw, sK + cur * G::kKStage, lane);
+      qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + cur * C::kKStage, lane);
       float alpha;
       u32x4 pb[4];
       if (kBlockKeys * (blk + 1) <= kfull) {
@@ -449,7 +568,7 @@ void prefill_kernel(const PrefillParams p) {
       } else {
         softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
       }
-      pv_accumulate<D, NT>(acc, 0, alpha, pb, sV + cur * G::kVStage, lane);
+      pv_accumulate<D, NT>(acc, 0, alpha, pb, sV + cur * C::kVStage, lane);
       if constexpr (!SPLIT) {
         if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) {
           // End of a 512-key chunk: fold its partial into the running total.
@@ -471,7 +590,7 @@ void prefill_kernel(const PrefillParams p) {
         if constexpr (C::kDirect) {
           wait_vm();
         } else {
-          rst.store(sK + (cur ^ 1) * G::kKStage, true, sV + (cur ^ 1) * G::kVStage, true, tid);
+          rst.store(sK + (cur ^ 1) * C::kKStage, true, sV + (cur ^ 1) * C::kVStage, true, tid);
         }
       }
       __syncthreads();
