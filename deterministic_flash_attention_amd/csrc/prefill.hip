@@ -363,6 +363,16 @@ void prefill_kernel(const PrefillParams p) {
 
   const int qrow = r0 + 32 * wave + (lane & 31);  // local query row of this lane
   const int lim = p.causal ? min(lk, qrow + koff + 1) : lk;
+  // Blocks [0, wblk_end) hold a key visible to some row of this wave; later
+  // blocks are fully masked for all of its rows (and a wave whose rows all lie
+  // past the sequence has no block).  Such a block leaves m, l and acc exactly
+  // as they were (alpha = 1, p = 0, and acc, which starts at +0, is never -0,
+  // so adding zero products changes no bit), so the wave skips its arithmetic
+  // while still taking part in the staging and the barriers.
+  const int wrow_last = min(r0 + 32 * (int)uniform(wave) + 31, lq - 1);
+  const int wlim = r0 + 32 * (int)uniform(wave) >= lq ? 0
+                   : (p.causal ? min(lk, wrow_last + koff + 1) : lk);
+  const int wblk_end = (wlim + kBlockKeys - 1) / kBlockKeys;
 
   if constexpr (SPLIT) {
     if (blk_begin >= blk_end) {
@@ -487,29 +497,32 @@ void prefill_kernel(const PrefillParams p) {
     u32x4 pb[4];
     for (int j = 0; j < n; ++j) {
       const int blk = blk_begin + j;
+      const bool live = blk < wblk_end;  // this wave computes block j
       __builtin_amdgcn_s_setprio(2);  // MFMA phase ahead of the other half's VALU
       if (j > 0) {
-        pv_mfma<D, NT>(acc, 0, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
+        if (blk - 1 < wblk_end) pv_mfma<D, NT>(acc, 0, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
         if constexpr (!SPLIT) {
           if (blk % kBlocksPerChunk == 0) fold_chunk();
         }
       }
       f32x16 s[2];
-      qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + (j & 1) * C::kKStage, lane);
+      if (live) qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + (j & 1) * C::kKStage, lane);
       __syncthreads();
       __builtin_amdgcn_s_setprio(0);
       event(j + lag);
-      float alpha;
-      if (kBlockKeys * (blk + 1) <= kfull) {
-        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
-      } else {
-        softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
+      if (live) {
+        float alpha;
+        if (kBlockKeys * (blk + 1) <= kfull) {
+          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+        } else {
+          softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
+        }
+        rescale_acc<NT>(acc, alpha);
       }
-      rescale_acc<NT>(acc, alpha);
       wait_vm();
       __syncthreads();
     }
-    pv_mfma<D, NT>(acc, 0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
+    if (blk_end - 1 < wblk_end) pv_mfma<D, NT>(acc, 0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
     if constexpr (!SPLIT) fold_chunk();
     if (!lag) __syncthreads();
       } else {
@@ -559,16 +572,18 @@ void prefill_kernel(const PrefillParams p) {
           reg_load(blk + 1);
         }
       }
-      f32x16 s[2];
-      qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + cur * C::kKStage, lane);
-      float alpha;
-      u32x4 pb[4];
-      if (kBlockKeys * (blk + 1) <= kfull) {
-        softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
-      } else {
-        softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
+      if (blk < wblk_end) {
+        f32x16 s[2];
+        qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + cur * C::kKStage, lane);
+        float alpha;
+        u32x4 pb[4];
+        if (kBlockKeys * (blk + 1) <= kfull) {
+          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+        } else {
+          softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
+        }
+        pv_accumulate<D, NT>(acc, 0, alpha, pb, sV + cur * C::kVStage, lane);
       }
-      pv_accumulate<D, NT>(acc, 0, alpha, pb, sV + cur * C::kVStage, lane);
       if constexpr (!SPLIT) {
         if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) {
           // End of a 512-key chunk: fold its partial into the running total.
