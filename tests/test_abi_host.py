@@ -139,6 +139,8 @@ def _extend_args(**over):
     (dict(num_pages=0), DA_EINVAL),
     (dict(page_stride=-5), DA_EINVAL),
     (dict(token_stride=4), DA_EINVAL),        # 8-byte stride is not a multiple of 16
+    (dict(token_stride=64), DA_EINVAL),       # tokens closer than one head row (D = 128)
+    (dict(token_stride=1 << 26), DA_EUNSUPPORTED),  # a page beyond 32-bit offsets
     (dict(cu_q=None), DA_EINVAL),
     (dict(table=None), DA_EINVAL),
     (dict(ctx=None), DA_EINVAL),
