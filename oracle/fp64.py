@@ -17,6 +17,10 @@ Readings of points the page leaves open (each restated in the design notes):
     L_q queries and L_k keys iff ``j < L_k and (not causal or j <= i + L_k - L_q)``;
     this is the only alignment under which a decode row equals the last prefill
     row, which the page requires;
+  * a sliding window (local attention; window-sized bounds, aiter MQA-logits
+    page) ``(w_left, w_right)``, -1 meaning unbounded on that side, adds
+    ``j >= i + L_k - L_q - w_left`` and ``j <= i + L_k - L_q + w_right`` on the
+    same bottom-right diagonal;
   * grouped-query attention maps query head h to key/value head
     ``h // (Hq // Hkv)`` (contiguous groups);
   * a row with no visible key returns O = 0 and lse = -inf;
@@ -77,12 +81,19 @@ def dequantize_e4m3(codes: np.ndarray, scale: float) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Mask (reading of "+ mask"; see module docstring)
 # ----------------------------------------------------------------------------
-def visible(rows: np.ndarray, lq: int, lk: int, causal: bool) -> np.ndarray:
+def visible(rows: np.ndarray, lq: int, lk: int, causal: bool,
+            window: Sequence[int] = (-1, -1)) -> np.ndarray:
     """Boolean [len(rows), lk]: key j visible from local query row i."""
     j = np.arange(lk)[None, :]
+    diag = np.asarray(rows)[:, None] + (lk - lq)  # the row's own position among the keys
     ok = j < lk
     if causal:
-        ok = ok & (j <= (np.asarray(rows)[:, None] + (lk - lq)))
+        ok = ok & (j <= diag)
+    wl, wr = int(window[0]), int(window[1])
+    if wl >= 0:
+        ok = ok & (j >= diag - wl)
+    if wr >= 0:
+        ok = ok & (j <= diag + wr)
     return np.broadcast_to(ok, (len(rows), lk)).copy()
 
 
@@ -100,7 +111,8 @@ def _check(q, k, v, cu_q, cu_k, hq, hkv):
 # Plain definition
 # ----------------------------------------------------------------------------
 def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, hq: int, hkv: int, scale: float,
-              causal: bool, rows: Optional[Sequence[int]] = None):
+              causal: bool, rows: Optional[Sequence[int]] = None,
+              window: Sequence[int] = (-1, -1)):
     """O = softmax(scale * Q K^T + mask) V for packed variable-length sequences.
 
     q: [total_q, Hq, D], k/v: [total_k, Hkv, D] (fp64 values of the stored inputs);
@@ -126,7 +138,7 @@ def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, hq: int, hkv: int, scale: flo
             rl = local[r0:r0 + _ROW_BLOCK]
             if len(rl) == 0:
                 continue
-            mask = visible(rl, lq, lk, causal)
+            mask = visible(rl, lq, lk, causal, window)
             has_key = mask.any(axis=1)
             for h in range(hq):
                 g = h // group
@@ -182,7 +194,7 @@ def _merge(total, part):
     return Mn, Ln, An
 
 
-def chunk_partials(qrows, kb, vb, rows_local, lq, lk, scale, causal):
+def chunk_partials(qrows, kb, vb, rows_local, lq, lk, scale, causal, window=(-1, -1)):
     """Per-chunk partial states (m_c, l_c, acc_c) for the given rows of one head.
 
     Each chunk c covers absolute keys [512c, 512c+512) and folds its 64-key blocks
@@ -190,7 +202,7 @@ def chunk_partials(qrows, kb, vb, rows_local, lq, lk, scale, causal):
     """
     n = len(rows_local)
     d = vb.shape[1]
-    mask = visible(rows_local, lq, lk, causal)
+    mask = visible(rows_local, lq, lk, causal, window)
     parts = []
     for c0 in range(0, lk, CHUNK_KEYS):
         st = (np.full(n, -np.inf), np.zeros(n), np.zeros((n, d)))
@@ -204,7 +216,7 @@ def chunk_partials(qrows, kb, vb, rows_local, lq, lk, scale, causal):
 
 
 def attention_chunked(q, k, v, cu_seqlens_q, cu_seqlens_k, hq: int, hkv: int, scale: float,
-                      causal: bool):
+                      causal: bool, window: Sequence[int] = (-1, -1)):
     """The chunked evaluation: partials per 512-key chunk, merged ascending, then
     O = A / L (0 for a row with no visible key) and lse = M + log L."""
     q, k, v, cu_q, cu_k = _check(q, k, v, cu_seqlens_q, cu_seqlens_k, hq, hkv)
@@ -221,7 +233,7 @@ def attention_chunked(q, k, v, cu_seqlens_q, cu_seqlens_k, hq: int, hkv: int, sc
         for h in range(hq):
             g = h // group
             parts = chunk_partials(q[q0:q1, h, :], k[k0:k1, g, :], v[k0:k1, g, :], rl, lq, lk,
-                                   scale, causal)
+                                   scale, causal, window)
             tot = (np.full(lq, -np.inf), np.zeros(lq), np.zeros((lq, d)))
             for p in parts:
                 tot = _merge(tot, p)
@@ -244,9 +256,10 @@ def gather_pages(cache, page_table_row, ctx: int, page_size: int):
 
 
 def paged_decode(q, k_cache, v_cache, page_table, context_lens, hq: int, hkv: int,
-                 scale: float, page_size: int):
+                 scale: float, page_size: int, window_left: int = -1):
     """Single-token decode: for sequence b the query is the last row of a
-    sequence of length ctx_b, so every cached key j < ctx_b is visible.
+    sequence of length ctx_b, so every cached key j < ctx_b is visible (with a
+    left window w, keys j >= ctx_b - 1 - w).
 
     q: [B, Hq, D]; caches: [pages, page_size, Hkv, D]; page_table: [B, max_pages].
     Returns (O [B, Hq, D], lse [B, Hq]) in fp64.
@@ -259,19 +272,38 @@ def paged_decode(q, k_cache, v_cache, page_table, context_lens, hq: int, hkv: in
         ctx = int(context_lens[b])
         kb = gather_pages(k_cache, page_table[b], ctx, page_size).astype(np.float64)
         vb = gather_pages(v_cache, page_table[b], ctx, page_size).astype(np.float64)
-        o, l = attention(q[b:b + 1], kb, vb, [0, 1], [0, ctx], hq, hkv, scale, causal=True)
+        o, l = attention(q[b:b + 1], kb, vb, [0, 1], [0, ctx], hq, hkv, scale, causal=True,
+                         window=(window_left, -1))
         out[b], lse[b] = o[0], l[0]
     return out, lse
 
 
-def attention_flops(seqlens_q, seqlens_k, hq: int, d: int, causal: bool) -> int:
+def attention_flops(seqlens_q, seqlens_k, hq: int, d: int, causal: bool,
+                    window: Sequence[int] = (-1, -1)) -> int:
     """Algorithmic FLOP count: 4*D per visible (query, key) pair per query head
     (2*D for q.k and 2*D for p*v).  Chunking adds no counted work."""
     total = 0
+    wl, wr = int(window[0]), int(window[1])
     for lq, lk in zip(seqlens_q, seqlens_k):
         lq, lk = int(lq), int(lk)
-        total += _causal_pairs(lq, lk) if causal else lq * lk
+        if wl < 0 and wr < 0:
+            total += _causal_pairs(lq, lk) if causal else lq * lk
+        else:
+            total += _window_pairs(lq, lk, causal, wl, wr)
     return 4 * d * hq * total
+
+
+def _window_pairs(lq: int, lk: int, causal: bool, wl: int, wr: int) -> int:
+    # per row i the visible keys form [max(0, i+off-wl), min(lk, i+off+1 or i+off+wr+1, lk))
+    off = lk - lq
+    i = np.arange(lq, dtype=np.int64)
+    lo = np.clip(i + off - wl, 0, lk) if wl >= 0 else np.zeros(lq, dtype=np.int64)
+    hi = np.full(lq, lk, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, np.clip(i + off + 1, 0, lk))
+    if wr >= 0:
+        hi = np.minimum(hi, np.clip(i + off + wr + 1, 0, lk))
+    return int(np.maximum(hi - lo, 0).sum())
 
 
 def _causal_pairs(lq: int, lk: int) -> int:

@@ -21,8 +21,10 @@ import oracle.fp64 as oatt
 RNG = np.random.default_rng(1234)
 
 
-def brute_force(q, k, v, cu_q, cu_k, hq, hkv, scale, causal):
-    """Textbook softmax attention with explicit Python loops and math.exp."""
+def brute_force(q, k, v, cu_q, cu_k, hq, hkv, scale, causal, window=(-1, -1)):
+    """Textbook softmax attention with explicit Python loops and math.exp.
+    window = (w_left, w_right), -1 unbounded: key j in [diag - w_left, diag + w_right]
+    around the row's bottom-right diagonal position diag = i + L_k - L_q."""
     tq, _, d = q.shape
     out = [[[0.0] * d for _ in range(hq)] for _ in range(tq)]
     lse = [[-math.inf] * hq for _ in range(tq)]
@@ -33,7 +35,11 @@ def brute_force(q, k, v, cu_q, cu_k, hq, hkv, scale, causal):
         for h in range(hq):
             g = h // grp
             for i in range(lq):
-                keys = [j for j in range(lk) if (not causal) or j <= i + lk - lq]
+                diag = i + lk - lq
+                keys = [j for j in range(lk)
+                        if ((not causal) or j <= diag)
+                        and (window[0] < 0 or j >= diag - window[0])
+                        and (window[1] < 0 or j <= diag + window[1])]
                 if not keys:
                     continue
                 s = []
@@ -271,6 +277,106 @@ def test_flop_counts():
 
 
 # ---------------------------------------------------------------------------
+# Sliding windows (local attention)
+# ---------------------------------------------------------------------------
+WINDOW_CASES = [
+    # (seqlens_q, seqlens_k, causal, window)
+    ([9], [9], True, (3, -1)),
+    ([9], [9], False, (2, 4)),
+    ([3, 9, 1], [3, 9, 1], True, (0, -1)),
+    ([2, 5], [6, 11], True, (4, -1)),       # extend with a window
+    ([6, 3], [4, 3], False, (1, 1)),        # q_len > k_len
+    ([8], [8], False, (-1, 2)),             # right window only
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES)
+def test_window_plain_matches_brute_force(case):
+    sq, sk, causal, win = case
+    q, k, v, cu_q, cu_k = make(sq, sk, 2, 1, 3, seed=sum(sk) + win[0] + 5 * win[1])
+    o, l = oracle.attention(q, k, v, cu_q, cu_k, 2, 1, 0.41, causal, window=win)
+    ob, lb = brute_force(q, k, v, cu_q, cu_k, 2, 1, 0.41, causal, window=win)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(l), np.isneginf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(l[fin], lb[fin], rtol=1e-12, atol=1e-13)
+
+
+def test_window_zero_left_causal_closed_form():
+    """With a left window of 0 under the causal mask each row sees exactly its
+    own diagonal key: O_i = V[i + L_k - L_q] and lse_i = scale * q_i . k_diag."""
+    sq, sk = [5, 4], [9, 4]
+    q, k, v, cu_q, cu_k = make(sq, sk, 2, 2, 6, seed=3)
+    o, l = oracle.attention(q, k, v, cu_q, cu_k, 2, 2, 0.5, True, window=(0, -1))
+    for b in range(2):
+        for i in range(sq[b]):
+            j = cu_k[b] + i + sk[b] - sq[b]
+            for h in range(2):
+                np.testing.assert_allclose(o[cu_q[b] + i, h], v[j, h], rtol=0, atol=1e-15)
+                np.testing.assert_allclose(l[cu_q[b] + i, h], 0.5 * q[cu_q[b] + i, h] @ k[j, h],
+                                           rtol=1e-14)
+
+
+def test_window_wide_equals_unwindowed():
+    q, k, v, cu_q, cu_k = make([37, 5], [90, 70], 2, 1, 4, seed=9)
+    for causal in (False, True):
+        o1, l1 = oracle.attention(q, k, v, cu_q, cu_k, 2, 1, 0.3, causal)
+        o2, l2 = oracle.attention(q, k, v, cu_q, cu_k, 2, 1, 0.3, causal, window=(500, 500))
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("win", [(100, -1), (700, -1), (64, 200)])
+def test_window_chunked_equals_plain(win):
+    """Windows that start and end inside chunks and blocks: the chunked
+    evaluation skips nothing it should not (leading fully masked chunks stay
+    empty) and equals the plain definition."""
+    q, k, v, cu_q, cu_k = make([1300, 70], [1300, 1100], 2, 1, 8, seed=21)
+    for causal in (False, True):
+        o1, l1 = oracle.attention(q, k, v, cu_q, cu_k, 2, 1, 0.35, causal, window=win)
+        o2, l2 = oracle.attention_chunked(q, k, v, cu_q, cu_k, 2, 1, 0.35, causal, window=win)
+        np.testing.assert_allclose(o2, o1, rtol=1e-11, atol=1e-12)
+        np.testing.assert_array_equal(np.isneginf(l1), np.isneginf(l2))
+
+
+def test_window_flop_counts_match_mask():
+    for sq, sk, causal, win in WINDOW_CASES + [([300], [300], True, (128, -1)),
+                                              ([70], [1100], False, (64, 200))]:
+        pairs = sum(int(oatt.visible(np.arange(a), a, b, causal, win).sum())
+                    for a, b in zip(sq, sk))
+        assert oracle.attention_flops(sq, sk, 3, 16, causal, window=win) == 4 * 16 * 3 * pairs
+
+
+def test_window_decode_is_last_row():
+    """A decode row with a left window equals the last row of the windowed
+    causal prefill of the same sequence."""
+    q, k, v, cu_q, cu_k = make([700], [700], 2, 1, 4, seed=5)
+    o, l = oracle.attention(q, k, v, cu_q, cu_k, 2, 1, 0.5, True, window=(200, -1))
+    page = 16
+    pad = np.full((704 - 700, 1, 4), np.nan)  # dead slots of the last page
+    kc = np.concatenate([k, pad]).reshape(-1, page, 1, 4)
+    vc = np.concatenate([v, pad]).reshape(-1, page, 1, 4)
+    table = np.arange(kc.shape[0])[None, :]
+    od, ld = oracle.paged_decode(q[-1:], kc, vc, table, [700], 2, 1, 0.5, page, window_left=200)
+    np.testing.assert_allclose(od[0], o[-1], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(ld[0], l[-1], rtol=1e-13)
+
+
+def test_planted_window_off_by_one(monkeypatch):
+    real = oatt.visible
+
+    def strict(rows, lq, lk, causal, window=(-1, -1)):
+        ok = real(rows, lq, lk, causal, window)
+        if window[0] >= 0:  # drop the window's first key
+            diag = np.asarray(rows)[:, None] + (lk - lq)
+            ok = ok & (np.arange(lk)[None, :] > diag - window[0])
+        return ok
+    monkeypatch.setattr(oatt, "visible", strict)
+    assert _fails(test_window_zero_left_causal_closed_form)
+    assert _fails(lambda: test_window_plain_matches_brute_force(WINDOW_CASES[0]))
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: each slip below is injected into the oracle (on the CPU) and
 # at least one pin above must fail on it.
 # ---------------------------------------------------------------------------
@@ -283,7 +389,7 @@ def _fails(fn):
 
 
 def test_planted_top_left_causal_alignment(monkeypatch):
-    def top_left(rows, lq, lk, causal):
+    def top_left(rows, lq, lk, causal, window=(-1, -1)):
         j = np.arange(lk)[None, :]
         ok = (j <= np.asarray(rows)[:, None]) if causal else (j < lk)
         return np.broadcast_to(ok, (len(rows), lk)).copy()
