@@ -109,7 +109,7 @@ def prefill_workload(cfg, causal, dtype, seed=0):
     return inp, t
 
 
-def run_prefill_fn(inp, t, schedule):
+def run_prefill_fn(inp, t, schedule, window=(-1, -1)):
     import torch
     import deterministic_flash_attention_amd as dfa
     tq, hq, d = inp.q.shape
@@ -119,20 +119,22 @@ def run_prefill_fn(inp, t, schedule):
 
     def fn():
         dfa.attn_prefill_fwd(t["q"], t["k"], t["v"], t["cq"], t["ck"], ms, mk, inp.scale,
-                             inp.causal, schedule, o=o, descales=desc)
+                             inp.causal, schedule, o=o, descales=desc, window=window)
     return fn, o
 
 
-def prefill_entry(name, cfg, causal, dtype, iters, warmup, peak, peak_note):
+def prefill_entry(name, cfg, causal, dtype, iters, warmup, peak, peak_note, window=(-1, -1)):
     import oracle
     inp, t = prefill_workload(cfg, causal, dtype)
-    fn, _ = run_prefill_fn(inp, t, 0)
+    fn, _ = run_prefill_fn(inp, t, 0, window)
     ms, _ = timed(fn, iters, warmup)
-    flops = oracle.attention_flops(cfg["seqlens"], cfg["seqlens"], cfg["hq"], cfg["d"], causal)
+    flops = oracle.attention_flops(cfg["seqlens"], cfg["seqlens"], cfg["hq"], cfg["d"], causal,
+                                   window=window)
     avg = sum(ms) / len(ms)
     tf = flops / (avg * 1e-3) / 1e12
     return {
         "workload": name, "causal": causal, "dtype": dtype, "seqlens": cfg["seqlens"],
+        "window": list(window),
         "hq": cfg["hq"], "hkv": cfg["hkv"], "d": cfg["d"], "flop": flops,
         "ms_mean": avg, "ms_min": min(ms), "value": tf, "unit": "TFLOP/s",
         "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
@@ -326,6 +328,9 @@ def main():
                                        20, 3, PEAK_BF16_TFLOPS, "bf16 dense MFMA"))
         secondary.append(decode_entry(20, 3))
         secondary.append(extend_entry(20, 3))
+        secondary.append(prefill_entry("sliding_window_1024", synth.DENSE_PREFILL, True, "bf16",
+                                       20, 3, PEAK_BF16_TFLOPS, "bf16 dense MFMA",
+                                       window=(1024, -1)))
         mixed = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
         for causal in (False, True):
             e = prefill_entry("fp8_wide_head", synth.FP8_WIDE, causal, "fp8", 20, 3, mixed,

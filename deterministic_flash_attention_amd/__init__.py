@@ -64,18 +64,18 @@ def load_library() -> ctypes.CDLL:
     lib.attn_partials_bytes.argtypes = [c_i64, c_i32, c_i32, c_i32]
     lib.attn_partials_bytes.restype = c_sz
     lib.attn_prefill_fwd.argtypes = [c_i32, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i64,
-                                     c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_f32, c_f32, c_f32,
-                                     c_i32, c_p, c_p, c_p, c_sz, c_p]
+                                     c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_i32,
+                                     c_f32, c_f32, c_f32, c_i32, c_p, c_p, c_p, c_sz, c_p]
     lib.attn_prefill_fwd.restype = ctypes.c_int
     lib.attn_decode_split_fwd.argtypes = [c_i32, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64, c_p,
                                           c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
-                                          c_f32, c_f32, c_f32, c_f32, c_i32, c_p, c_sz, c_p, c_p,
-                                          c_p]
+                                          c_i32, c_f32, c_f32, c_f32, c_f32, c_i32, c_p, c_sz,
+                                          c_p, c_p, c_p]
     lib.attn_decode_split_fwd.restype = ctypes.c_int
     lib.attn_paged_extend_fwd.argtypes = [c_i32, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64,
                                           c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i64, c_i32,
-                                          c_i32, c_i32, c_i32, c_f32, c_i32, c_f32, c_f32, c_f32,
-                                          c_i32, c_p, c_p, c_p, c_sz, c_p]
+                                          c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_f32,
+                                          c_f32, c_f32, c_i32, c_p, c_p, c_p, c_sz, c_p]
     lib.attn_paged_extend_fwd.restype = ctypes.c_int
     lib.attn_chunk_merge.argtypes = [c_p, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p]
     lib.attn_chunk_merge.restype = ctypes.c_int
@@ -127,22 +127,23 @@ def attn_partials_bytes(rows: int, num_heads_q: int, max_chunks: int, head_dim: 
 def attn_prefill_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                      softmax_scale: float, causal: bool, schedule: int = MONOLITHIC,
                      o=None, lse=None, partials=None, descales=(1.0, 1.0, 1.0),
-                     stream=None) -> None:
+                     window=(-1, -1), stream=None) -> None:
     """Mirror of the C ``attn_prefill_fwd``; outputs are caller-provided tensors."""
     lib = load_library()
     st = lib.attn_prefill_fwd(
         _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
         int(cu_seqlens_q.numel() - 1), int(max_seqlen_q), int(max_seqlen_k), int(q.shape[0]),
         int(k.shape[0]), int(q.shape[1]), int(k.shape[1]), int(q.shape[2]), float(softmax_scale),
-        int(bool(causal)), float(descales[0]), float(descales[1]), float(descales[2]),
-        int(schedule), _ptr(o), _ptr(lse), _ptr(partials),
+        int(bool(causal)), int(window[0]), int(window[1]), float(descales[0]), float(descales[1]),
+        float(descales[2]), int(schedule), _ptr(o), _ptr(lse), _ptr(partials),
         0 if partials is None else partials.numel() * partials.element_size(), _stream(stream))
     _check("attn_prefill_fwd", st)
 
 
 def attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
                           softmax_scale: float, schedule: int = SPLIT, partials=None, o=None,
-                          lse=None, descales=(1.0, 1.0, 1.0), stream=None) -> None:
+                          lse=None, descales=(1.0, 1.0, 1.0), window_left: int = -1,
+                          stream=None) -> None:
     """Mirror of the C ``attn_decode_split_fwd`` for caches shaped
     [num_pages, 16, Hkv, D] (contiguous)."""
     lib = load_library()
@@ -150,8 +151,9 @@ def attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_con
     st = lib.attn_decode_split_fwd(
         _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(npages),
         int(psize * hkv * d), int(hkv * d), int(d), _ptr(page_table), int(page_table.shape[1]),
-        _ptr(context_lens), int(max_context_len), int(q.shape[0]), int(psize), int(q.shape[1]),
-        int(hkv), int(d), float(softmax_scale), float(descales[0]), float(descales[1]),
+        _ptr(context_lens), int(max_context_len), int(window_left), int(q.shape[0]), int(psize),
+        int(q.shape[1]), int(hkv), int(d), float(softmax_scale), float(descales[0]),
+        float(descales[1]),
         float(descales[2]), int(schedule), _ptr(partials),
         0 if partials is None else partials.numel() * partials.element_size(), _ptr(o),
         _ptr(lse), _stream(stream))
@@ -161,7 +163,8 @@ def attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_con
 def attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
                           max_seqlen_q: int, max_context_len: int, softmax_scale: float,
                           causal: bool, schedule: int = MONOLITHIC, o=None, lse=None,
-                          partials=None, descales=(1.0, 1.0, 1.0), stream=None) -> None:
+                          partials=None, descales=(1.0, 1.0, 1.0), window=(-1, -1),
+                          stream=None) -> None:
     """Mirror of the C ``attn_paged_extend_fwd`` for caches shaped
     [num_pages, 16, Hkv, D] (contiguous)."""
     lib = load_library()
@@ -171,8 +174,9 @@ def attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context
         int(psize * hkv * d), int(hkv * d), int(d), _ptr(page_table), int(page_table.shape[1]),
         _ptr(context_lens), int(cu_seqlens_q.numel() - 1), int(max_seqlen_q),
         int(max_context_len), int(q.shape[0]), int(psize), int(q.shape[1]), int(hkv), int(d),
-        float(softmax_scale), int(bool(causal)), float(descales[0]), float(descales[1]),
-        float(descales[2]), int(schedule), _ptr(o), _ptr(lse), _ptr(partials),
+        float(softmax_scale), int(bool(causal)), int(window[0]), int(window[1]),
+        float(descales[0]), float(descales[1]), float(descales[2]), int(schedule), _ptr(o),
+        _ptr(lse), _ptr(partials),
         0 if partials is None else partials.numel() * partials.element_size(), _stream(stream))
     _check("attn_paged_extend_fwd", st)
 
@@ -197,7 +201,7 @@ def _new_partials(rows: int, hq: int, cmax: int, d: int, device) -> torch.Tensor
 def prefill(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
             causal: bool, softmax_scale: Optional[float] = None, schedule: int = MONOLITHIC,
             descales=(1.0, 1.0, 1.0), out: Optional[torch.Tensor] = None,
-            return_lse: bool = False, stream=None):
+            return_lse: bool = False, window=(-1, -1), stream=None):
     """Packed-varlen attention forward; returns O (bf16) and optionally lse.
 
     With ``schedule=SPLIT`` the chunk partials go to a workspace and
@@ -212,19 +216,20 @@ def prefill(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k
         part = _new_partials(tq, hq, cmax, d, q.device)
         attn_prefill_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                          softmax_scale, causal, SPLIT, partials=part, descales=descales,
-                         stream=stream)
+                         window=window, stream=stream)
         attn_chunk_merge(part, tq, hq, cmax, d, o, lse, v_descale=descales[2], stream=stream)
     else:
         attn_prefill_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                          softmax_scale, causal, MONOLITHIC, o=o, lse=lse, descales=descales,
-                         stream=stream)
+                         window=window, stream=stream)
     return (o, lse) if return_lse else o
 
 
 def decode(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
            softmax_scale: Optional[float] = None, schedule: int = SPLIT,
            descales=(1.0, 1.0, 1.0), out: Optional[torch.Tensor] = None,
-           return_lse: bool = False, partials: Optional[torch.Tensor] = None, stream=None):
+           return_lse: bool = False, partials: Optional[torch.Tensor] = None,
+           window_left: int = -1, stream=None):
     """Single-token paged decode; returns O (bf16) and optionally lse."""
     b, hq, d = q.shape
     if softmax_scale is None:
@@ -236,19 +241,20 @@ def decode(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
         part = partials if partials is not None else _new_partials(b, hq, cmax, d, q.device)
         attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len,
                               softmax_scale, SPLIT, partials=part, descales=descales,
-                              stream=stream)
+                              window_left=window_left, stream=stream)
         attn_chunk_merge(part, b, hq, cmax, d, o, lse, v_descale=descales[2], stream=stream)
     else:
         attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len,
                               softmax_scale, MONOLITHIC, o=o, lse=lse, descales=descales,
-                              stream=stream)
+                              window_left=window_left, stream=stream)
     return (o, lse) if return_lse else o
 
 
 def paged_extend(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens, max_seqlen_q: int,
                  max_context_len: int, causal: bool, softmax_scale: Optional[float] = None,
                  schedule: int = MONOLITHIC, descales=(1.0, 1.0, 1.0),
-                 out: Optional[torch.Tensor] = None, return_lse: bool = False, stream=None):
+                 out: Optional[torch.Tensor] = None, return_lse: bool = False, window=(-1, -1),
+                 stream=None):
     """Mixed prefill / extend / decode batch over a paged KV cache; returns O
     (bf16) and optionally lse.  Sequence b's rows are its last
     cu_seqlens_q[b+1] - cu_seqlens_q[b] tokens of context_lens[b]."""
@@ -262,10 +268,10 @@ def paged_extend(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens, ma
         part = _new_partials(tq, hq, cmax, d, q.device)
         attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
                               max_seqlen_q, max_context_len, softmax_scale, causal, SPLIT,
-                              partials=part, descales=descales, stream=stream)
+                              partials=part, descales=descales, window=window, stream=stream)
         attn_chunk_merge(part, tq, hq, cmax, d, o, lse, v_descale=descales[2], stream=stream)
     else:
         attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
                               max_seqlen_q, max_context_len, softmax_scale, causal, MONOLITHIC,
-                              o=o, lse=lse, descales=descales, stream=stream)
+                              o=o, lse=lse, descales=descales, window=window, stream=stream)
     return (o, lse) if return_lse else o

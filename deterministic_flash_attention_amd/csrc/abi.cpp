@@ -65,12 +65,14 @@ da_status attn_prefill_fwd(int32_t dtype, const void* q, const void* k, const vo
                            int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                            int64_t total_q, int64_t total_k, int32_t num_heads_q,
                            int32_t num_heads_kv, int32_t head_dim, float softmax_scale,
-                           int32_t causal, float q_descale, float k_descale, float v_descale,
+                           int32_t causal, int32_t window_left, int32_t window_right,
+                           float q_descale, float k_descale, float v_descale,
                            int32_t schedule, void* o, float* lse, float* partials,
                            size_t partials_bytes, void* stream) {
   if (dtype != DA_BF16 && dtype != DA_FP8_E4M3) return DA_EINVAL;
   if (schedule != DA_MONOLITHIC && schedule != DA_SPLIT) return DA_EINVAL;
   if (causal != 0 && causal != 1) return DA_EINVAL;
+  if (window_left < -1 || window_right < -1) return DA_EINVAL;
   if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
     return DA_EINVAL;
   if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return DA_EINVAL;
@@ -116,6 +118,8 @@ da_status attn_prefill_fwd(int32_t dtype, const void* q, const void* k, const vo
   p.tiles = tiles;
   p.cmax = cmax;
   p.causal = causal;
+  p.window_left = window_left;
+  p.window_right = window_right;
   p.c_scale = score_constant(softmax_scale, q_descale, k_descale);
   p.v_descale = v_descale;
   const hipError_t e = detattn::launch_prefill(p, head_dim, dtype == DA_FP8_E4M3, split, false,
@@ -130,12 +134,14 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
                                 const int32_t* context_lens, int32_t batch, int32_t max_seqlen_q,
                                 int32_t max_context_len, int64_t total_q, int32_t page_size,
                                 int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                                float softmax_scale, int32_t causal, float q_descale,
-                                float k_descale, float v_descale, int32_t schedule, void* o,
-                                float* lse, float* partials, size_t partials_bytes, void* stream) {
+                                float softmax_scale, int32_t causal, int32_t window_left,
+                                int32_t window_right, float q_descale, float k_descale,
+                                float v_descale, int32_t schedule, void* o, float* lse,
+                                float* partials, size_t partials_bytes, void* stream) {
   if (dtype != DA_BF16 && dtype != DA_FP8_E4M3) return DA_EINVAL;
   if (schedule != DA_MONOLITHIC && schedule != DA_SPLIT) return DA_EINVAL;
   if (causal != 0 && causal != 1) return DA_EINVAL;
+  if (window_left < -1 || window_right < -1) return DA_EINVAL;
   if (batch < 0 || max_seqlen_q < 0 || max_context_len < 0 || total_q < 0) return DA_EINVAL;
   if (max_pages_per_seq <= 0 || num_pages <= 0) return DA_EINVAL;
   if (page_stride <= 0 || token_stride <= 0 || head_stride <= 0) return DA_EINVAL;
@@ -186,6 +192,8 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
   p.tiles = tiles;
   p.cmax = cmax;
   p.causal = causal;
+  p.window_left = window_left;
+  p.window_right = window_right;
   p.c_scale = score_constant(softmax_scale, q_descale, k_descale);
   p.v_descale = v_descale;
   p.page_table = page_table;
@@ -205,13 +213,14 @@ da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cach
                                 int64_t token_stride, int64_t head_stride,
                                 const int32_t* page_table, int32_t max_pages_per_seq,
                                 const int32_t* context_lens, int32_t max_context_len,
-                                int32_t batch, int32_t page_size, int32_t num_heads_q,
-                                int32_t num_heads_kv, int32_t head_dim, float softmax_scale,
-                                float q_descale, float k_descale, float v_descale,
-                                int32_t schedule, float* partials, size_t partials_bytes,
-                                void* o, float* lse, void* stream) {
+                                int32_t window_left, int32_t batch, int32_t page_size,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                float softmax_scale, float q_descale, float k_descale,
+                                float v_descale, int32_t schedule, float* partials,
+                                size_t partials_bytes, void* o, float* lse, void* stream) {
   if (dtype != DA_BF16 && dtype != DA_FP8_E4M3) return DA_EINVAL;
   if (schedule != DA_MONOLITHIC && schedule != DA_SPLIT) return DA_EINVAL;
+  if (window_left < -1) return DA_EINVAL;
   if (batch < 0 || max_context_len < 0 || max_pages_per_seq <= 0 || num_pages <= 0) return DA_EINVAL;
   if (page_stride <= 0 || token_stride <= 0 || head_stride <= 0) return DA_EINVAL;
   if (num_heads_q <= 0 || num_heads_kv <= 0 || num_heads_q % num_heads_kv != 0) return DA_EINVAL;
@@ -256,6 +265,7 @@ da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cach
   p.group = num_heads_q / num_heads_kv;
   p.max_pages = max_pages_per_seq;
   p.cmax = cmax;
+  p.window_left = window_left;
   p.c_scale = score_constant(softmax_scale, q_descale, k_descale);
   p.v_descale = v_descale;
   const hipError_t e = detattn::launch_decode(p, head_dim, dtype == DA_FP8_E4M3, split,

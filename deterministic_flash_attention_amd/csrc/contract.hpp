@@ -130,12 +130,15 @@ __device__ __forceinline__ float half_wave_sum(float x) {
   return bits_f32(r[0]) + bits_f32(r[1]);
 }
 
+// Masking of a block: none, keys at block offset >= rel_hi, or keys outside
+// [rel_lo, rel_hi) (a sliding window's lower edge).
+enum BlockMask { kNoMask = 0, kMaskHi = 1, kMaskLoHi = 2 };
+
 // Online-softmax update of one lane's query column over a 64-key block.
-// rel_lim: keys at block offset >= rel_lim are masked (MASKED blocks only).
 // Returns alpha for the accumulator and P^T as four bf16x8 PV operands.
-template <bool MASKED>
-__device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float c, int rel_lim,
-                                              float& m, float& l, float& alpha,
+template <int MASK>
+__device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float c, int rel_lo,
+                                              int rel_hi, float& m, float& l, float& alpha,
                                               u32x4 (&pb)[4]) {
   // Phases 0-1: mask by select and row max on the raw dot products.  fl(c*s)
   // is monotonic in s for c > 0, so fl(c * max s) is exactly the max of the
@@ -145,14 +148,22 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float v = s[0][i];
-    if (MASKED) v = (score_key(0, i, h) < rel_lim) ? v : -INFINITY;
+    if (MASK == kMaskHi) v = (score_key(0, i, h) < rel_hi) ? v : -INFINITY;
+    if (MASK == kMaskLoHi) {
+      const int key = score_key(0, i, h);
+      v = (key >= rel_lo && key < rel_hi) ? v : -INFINITY;
+    }
     x[0][i] = v;
     mr0 = fmaxf(mr0, v);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float v = s[1][i];
-    if (MASKED) v = (score_key(1, i, h) < rel_lim) ? v : -INFINITY;
+    if (MASK == kMaskHi) v = (score_key(1, i, h) < rel_hi) ? v : -INFINITY;
+    if (MASK == kMaskLoHi) {
+      const int key = score_key(1, i, h);
+      v = (key >= rel_lo && key < rel_hi) ? v : -INFINITY;
+    }
     x[1][i] = v;
     mr1 = fmaxf(mr1, v);
   }

@@ -125,7 +125,12 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
   ctx = max(0, min(ctx, p.max_pages * kPageSize));
   const int nblk = (ctx + kBlockKeys - 1) / kBlockKeys;
   const int nch = (ctx + kChunkKeys - 1) / kChunkKeys;
-  int blk_begin = 0, blk_end = nblk;
+  // A left window keeps keys [lo, ctx) (the row is the sequence's last token):
+  // blocks and chunks wholly below lo are skipped, and their partials are empty.
+  const int lo = p.window_left >= 0 ? max(0, ctx - 1 - p.window_left) : 0;
+  const int blk_first = lo / kBlockKeys;
+  const int chunk_first = blk_first / kBlocksPerChunk;
+  int blk_begin = blk_first, blk_end = nblk;
   const int64_t row_head = (int64_t)b * p.hq + (int64_t)g * grp;  // first query head of the group
   const bool ml_writer = (wave == 0) && (h == 0);
   const int64_t chunk_rows = (int64_t)p.batch * p.hq;  // (row, head) slots per chunk
@@ -139,9 +144,11 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
   if constexpr (SPLIT) {
     const int c0 = cgrp * kSplitChunks;
     const int c1 = min(c0 + kSplitChunks, p.cmax);
-    // Chunks past the context hold empty partials (m, l) = (-inf, 0).
-    for (int cc = max(c0, nch); cc < c1; ++cc) store_ml(cc, -INFINITY, 0.0f);
-    blk_begin = c0 * kBlocksPerChunk;
+    // Chunks past the context, or below the window, hold empty partials
+    // (m, l) = (-inf, 0).
+    for (int cc = c0; cc < c1; ++cc)
+      if (cc >= nch || cc < chunk_first) store_ml(cc, -INFINITY, 0.0f);
+    blk_begin = max(c0 * kBlocksPerChunk, blk_first);
     blk_end = min(c1 * kBlocksPerChunk, nblk);
     if (blk_begin >= blk_end) return;
   }
@@ -211,10 +218,13 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
         qk_scores_qrow<D, FP8>(s, qrow, ks, lane);
         float alpha;
         u32x4 pb[4];
-        if (kBlockKeys * (blk + 1) <= ctx) {
-          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
+        const int b0 = kBlockKeys * blk;
+        if (b0 >= lo && b0 + kBlockKeys <= ctx) {
+          softmax_block<kNoMask>(s, h, c, 0, 0, m, l, alpha, pb);
+        } else if (b0 >= lo) {
+          softmax_block<kMaskHi>(s, h, c, 0, ctx - b0, m, l, alpha, pb);
         } else {
-          softmax_block<true>(s, h, c, ctx - kBlockKeys * blk, m, l, alpha, pb);
+          softmax_block<kMaskLoHi>(s, h, c, lo - b0, ctx - b0, m, l, alpha, pb);
         }
         pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
         if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);

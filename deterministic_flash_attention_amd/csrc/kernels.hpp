@@ -24,6 +24,8 @@ struct PrefillParams {
   int32_t tiles;      // ceil(max_seqlen_q / tile rows)
   int32_t cmax;       // ceil(max_seqlen_k / 512)
   int32_t causal;
+  int32_t window_left;   // sliding window on the bottom-right diagonal; -1 unbounded
+  int32_t window_right;
   float c_scale;      // softmax_scale * q_descale * k_descale * log2(e)
   float v_descale;
   // Paged K/V (paged extend): k and v are the page caches, keys of sequence b
@@ -57,6 +59,7 @@ struct DecodeParams {
   int32_t group;          // hq / hkv
   int32_t max_pages;
   int32_t cmax;           // ceil(max_context_len / 512)
+  int32_t window_left;    // keys j >= ctx - 1 - window_left; -1 unbounded
   float c_scale;
   float v_descale;
 };

@@ -83,8 +83,10 @@ struct KVStager {
       const int x = tid + u * C::kThreads;
       if (C::kPerThread * C::kThreads == C::kBlockChunks || x < C::kBlockChunks) {
         const int r = x / G::kChunks16, col = x % G::kChunks16;
-        if (kon) kreg[u] = buf_load16(kr, (uint32_t)(kkey0 + r) * row_bytes + (uint32_t)col * 16u);
-        if (von) vreg[u] = buf_load16(vr, (uint32_t)(vkey0 + r) * row_bytes + (uint32_t)col * 16u);
+        // kkey0 / vkey0 are relative to the descriptors' base row and may be
+        // negative; the offset then wraps past every descriptor (zeros).
+        if (kon) kreg[u] = buf_load16(kr, (uint32_t)((int64_t)(kkey0 + r) * row_bytes) + (uint32_t)col * 16u);
+        if (von) vreg[u] = buf_load16(vr, (uint32_t)((int64_t)(vkey0 + r) * row_bytes) + (uint32_t)col * 16u);
       }
     }
   }
@@ -159,26 +161,37 @@ struct DirectStager {
   uint32_t voff[kVPer];
   rsrc_t kr, vr;
   uint32_t row_bytes;
+  int kbase;  // key row at which the descriptors start
 
   static __device__ __forceinline__ uint32_t slot_offset(int seg, int lane, int slots,
                                                          uint32_t row_bytes) {
     const int s = 64 * seg + lane, row = s / slots, c = s % slots;
     return c < G::kChunks16 ? (uint32_t)row * row_bytes + 16u * (uint32_t)c : kParked;
   }
-  __device__ __forceinline__ void init(int wave, int lane, rsrc_t k, rsrc_t v, uint32_t rb) {
+  __device__ __forceinline__ void init(int wave, int lane, rsrc_t k, rsrc_t v, uint32_t rb,
+                                       int base) {
     kr = k;
     vr = v;
     row_bytes = rb;
+    kbase = base;
 #pragma unroll
     for (int u = 0; u < kKPer; ++u) koff[u] = slot_offset(wave + u * NW, lane, kKSlots, rb);
 #pragma unroll
     for (int u = 0; u < kVPer; ++u) voff[u] = slot_offset(wave + u * NW, lane, kVSlots, rb);
   }
   __device__ __forceinline__ void prefetch(int, int) {}  // nothing to look up
-  // The block offset (first key times the row stride) is below 2^31, so a
-  // parked offset plus it stays out of range without wrapping.
+  // Byte offset of block blk's first row from the descriptors' base row kbase.
+  // It is negative (wrapping to a huge unsigned value) for the block holding
+  // kbase when kbase is not block-aligned: rows below kbase then fail the range
+  // check and read zeros, which is the window's lower bound done in hardware.
+  // Pad lanes add it to the constant parked offset, never to a multiple of the
+  // window: 0x80000000 - 63 rows stays past every descriptor, because key rows
+  // (plus a block) fit 31 bits.
+  __device__ __forceinline__ uint32_t block_offset(int blk) const {
+    return (uint32_t)((int64_t)(blk * kBlockKeys - kbase) * row_bytes);
+  }
   __device__ __forceinline__ void issue_k(int blk, unsigned char* ks, int wave) const {
-    const uint32_t blk_off = (uint32_t)(blk * kBlockKeys) * row_bytes;
+    const uint32_t blk_off = block_offset(blk);
 #pragma unroll
     for (int u = 0; u < kKPer; ++u) {
       const int seg = wave + u * NW;
@@ -186,7 +199,7 @@ struct DirectStager {
     }
   }
   __device__ __forceinline__ void issue_v(int blk, unsigned char* vs, int wave) const {
-    const uint32_t blk_off = (uint32_t)(blk * kBlockKeys) * row_bytes;
+    const uint32_t blk_off = block_offset(blk);
 #pragma unroll
     for (int u = 0; u < kVPer; ++u) {
       const int seg = wave + u * NW;
@@ -349,30 +362,49 @@ void prefill_kernel(const PrefillParams p) {
   const int r0 = tile * C::kTileRows;
   const int g = head / (p.hq / p.hkv);
 
-  // Key ranges of this tile (bottom-right causal alignment).
+  // Visible keys of local query row i: [row_lo(i), row_hi(i)), bounds on the
+  // bottom-right diagonal i + koff (causal, and a sliding window's left and
+  // right edges).  Both bounds are nondecreasing in i.
   const int koff = lk - lq;
+  const int wl = p.window_left, wr = p.window_right;
+  auto row_lo = [&](int i) { return wl >= 0 ? max(0, i + koff - wl) : 0; };
+  auto row_hi = [&](int i) {
+    int hi = lk;
+    if (p.causal) hi = min(hi, i + koff + 1);
+    if (wr >= 0) hi = min(hi, i + koff + wr + 1);
+    return max(hi, 0);
+  };
+  // Key ranges of this tile's real rows.
   const int last = min(r0 + C::kTileRows, lq) - 1;
-  const int kend = p.causal ? min(lk, last + koff + 1) : lk;  // visible to some real row
-  const int kfull = p.causal ? min(lk, r0 + koff + 1) : lk;   // visible to every real row
-  const int nblk = kend > 0 ? (kend + kBlockKeys - 1) / kBlockKeys : 0;
-  int blk_begin = 0, blk_end = nblk;
+  const int kstart = row_lo(r0);    // first key visible to some row
+  const int kend = row_hi(last);    // past the last key visible to some row
+  const int klo_full = row_lo(last);  // keys in [klo_full, kfull) are visible to every row
+  const int kfull = row_hi(r0);
+  const int nblk = kend > kstart ? (kend + kBlockKeys - 1) / kBlockKeys : 0;
+  const int blk_first = kend > kstart ? kstart / kBlockKeys : 0;
+  int blk_begin = blk_first, blk_end = nblk;
   if constexpr (SPLIT) {
-    blk_begin = chunk * kBlocksPerChunk;
-    blk_end = min(blk_begin + kBlocksPerChunk, nblk);
+    blk_begin = max(chunk * kBlocksPerChunk, blk_first);
+    blk_end = min(chunk * kBlocksPerChunk + kBlocksPerChunk, nblk);
   }
 
   const int qrow = r0 + 32 * wave + (lane & 31);  // local query row of this lane
-  const int lim = p.causal ? min(lk, qrow + koff + 1) : lk;
-  // Blocks [0, wblk_end) hold a key visible to some row of this wave; later
-  // blocks are fully masked for all of its rows (and a wave whose rows all lie
-  // past the sequence has no block).  Such a block leaves m, l and acc exactly
-  // as they were (alpha = 1, p = 0, and acc, which starts at +0, is never -0,
-  // so adding zero products changes no bit), so the wave skips its arithmetic
+  const int lo = row_lo(qrow), hi = row_hi(qrow);
+  // Blocks [wblk_first, wblk_end) hold a key visible to some row of this wave;
+  // the others are fully masked for all of its rows (a wave whose rows all lie
+  // past the sequence has none).  Such a block leaves m, l and acc exactly as
+  // they were (alpha = 1, p = 0, and acc, which starts at +0, is never -0, so
+  // adding zero products changes no bit), so the wave skips its arithmetic
   // while still taking part in the staging and the barriers.
-  const int wrow_last = min(r0 + 32 * (int)uniform(wave) + 31, lq - 1);
-  const int wlim = r0 + 32 * (int)uniform(wave) >= lq ? 0
-                   : (p.causal ? min(lk, wrow_last + koff + 1) : lk);
-  const int wblk_end = (wlim + kBlockKeys - 1) / kBlockKeys;
+  const int wrow0 = r0 + 32 * (int)uniform(wave);
+  const int wrow_last = min(wrow0 + 31, lq - 1);
+  const bool wactive = wrow0 < lq;
+  const int wlo = wactive ? row_lo(wrow0) : 0;
+  const int wlo_max = wactive ? row_lo(wrow_last) : 0;  // a lower edge masks blocks below it
+  const int whi = wactive ? row_hi(wrow_last) : 0;
+  const int wblk_first = wlo / kBlockKeys;
+  const int wblk_end = whi > wlo ? (whi + kBlockKeys - 1) / kBlockKeys : 0;
+  auto wave_live = [&](int blk) { return blk >= wblk_first && blk < wblk_end; };
 
   if constexpr (SPLIT) {
     if (blk_begin >= blk_end) {
@@ -398,6 +430,18 @@ void prefill_kernel(const PrefillParams p) {
       acc[j][i] = 0.0f;
       A[j][i] = 0.0f;
     }
+  // Softmax update of block blk, masked according to its class for this tile
+  // and wave.
+  auto softmax = [&](int blk, const f32x16 (&s)[2], float& alpha, u32x4 (&pb)[4]) {
+    const int b0 = kBlockKeys * blk;
+    if (b0 >= klo_full && b0 + kBlockKeys <= kfull) {
+      softmax_block<kNoMask>(s, h, c, 0, 0, m, l, alpha, pb);
+    } else if (b0 >= wlo_max) {
+      softmax_block<kMaskHi>(s, h, c, 0, hi - b0, m, l, alpha, pb);
+    } else {
+      softmax_block<kMaskLoHi>(s, h, c, lo - b0, hi - b0, m, l, alpha, pb);
+    }
+  };
 
   if (blk_begin < blk_end) {
     const int64_t q_head = (int64_t)q_start * p.hq + head;
@@ -409,10 +453,15 @@ void prefill_kernel(const PrefillParams p) {
     const unsigned char* vb = static_cast<const unsigned char*>(p.v) + kv_head * G::kRowBytes;
     const rsrc_t qr = make_rsrc(qb, extent_bytes(lq, q_row_bytes, G::kRowBytes,
                                                  (p.total_q * p.hq - q_head) * G::kRowBytes));
-    const uint32_t kv_ext = extent_bytes(lk, kv_row_bytes, G::kRowBytes,
-                                         (p.total_k * p.hkv - kv_head) * G::kRowBytes);
-    const rsrc_t kr = make_rsrc(kb, PAGED ? 0u : kv_ext);
-    const rsrc_t vr = make_rsrc(vb, PAGED ? 0u : kv_ext);
+    // Window-sized K/V descriptors: they cover key rows [kstart, kend) of the
+    // sequence, the keys some row of this tile can see (aiter MQA-logits page:
+    // num_records is the window test), so keys outside read as zeros.
+    const uint32_t kv_ext =
+        extent_bytes(kend - kstart, kv_row_bytes, G::kRowBytes,
+                     (p.total_k * p.hkv - kv_head) * G::kRowBytes - (int64_t)kstart * kv_row_bytes);
+    const int64_t kv_win = (int64_t)kstart * kv_row_bytes;
+    const rsrc_t kr = make_rsrc(kb + (PAGED ? 0 : kv_win), PAGED ? 0u : kv_ext);
+    const rsrc_t vr = make_rsrc(vb + (PAGED ? 0 : kv_win), PAGED ? 0u : kv_ext);
     // Paged caches: the kv head's slot-0 offset of a page, -1 outside the cache.
     const int32_t* const table = PAGED ? p.page_table + (int64_t)b * p.max_pages : nullptr;
     auto page_base = [&](int j) -> int64_t {
@@ -433,7 +482,7 @@ void prefill_kernel(const PrefillParams p) {
         return st;
       } else {
         DirectStager<D, NW> st;
-        st.init(wv, lane, kr, vr, kv_row_bytes);
+        st.init(wv, lane, kr, vr, kv_row_bytes, kstart);
         return st;
       }
     };
@@ -497,10 +546,10 @@ void prefill_kernel(const PrefillParams p) {
     u32x4 pb[4];
     for (int j = 0; j < n; ++j) {
       const int blk = blk_begin + j;
-      const bool live = blk < wblk_end;  // this wave computes block j
+      const bool live = wave_live(blk);  // this wave computes block j
       __builtin_amdgcn_s_setprio(2);  // MFMA phase ahead of the other half's VALU
       if (j > 0) {
-        if (blk - 1 < wblk_end) pv_mfma<D, NT>(acc, 0, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
+        if (wave_live(blk - 1)) pv_mfma<D, NT>(acc, 0, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
         if constexpr (!SPLIT) {
           if (blk % kBlocksPerChunk == 0) fold_chunk();
         }
@@ -512,17 +561,13 @@ void prefill_kernel(const PrefillParams p) {
       event(j + lag);
       if (live) {
         float alpha;
-        if (kBlockKeys * (blk + 1) <= kfull) {
-          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
-        } else {
-          softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
-        }
+        softmax(blk, s, alpha, pb);
         rescale_acc<NT>(acc, alpha);
       }
       wait_vm();
       __syncthreads();
     }
-    if (blk_end - 1 < wblk_end) pv_mfma<D, NT>(acc, 0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
+    if (wave_live(blk_end - 1)) pv_mfma<D, NT>(acc, 0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
     if constexpr (!SPLIT) fold_chunk();
     if (!lag) __syncthreads();
       } else {
@@ -533,7 +578,8 @@ void prefill_kernel(const PrefillParams p) {
         rst.load_paged(static_cast<const unsigned char*>(p.k), static_cast<const unsigned char*>(p.v),
                        blk * kBlockKeys, lk, p.token_stride, page_base, tid);
       } else {
-        rst.load(kr, blk * kBlockKeys, true, vr, blk * kBlockKeys, true, kv_row_bytes, tid);
+        rst.load(kr, blk * kBlockKeys - kstart, true, vr, blk * kBlockKeys - kstart, true,
+                 kv_row_bytes, tid);
       }
     };
     auto dst = make_direct();
@@ -572,16 +618,12 @@ void prefill_kernel(const PrefillParams p) {
           reg_load(blk + 1);
         }
       }
-      if (blk < wblk_end) {
+      if (wave_live(blk)) {
         f32x16 s[2];
         qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + cur * C::kKStage, lane);
         float alpha;
         u32x4 pb[4];
-        if (kBlockKeys * (blk + 1) <= kfull) {
-          softmax_block<false>(s, h, c, 0, m, l, alpha, pb);
-        } else {
-          softmax_block<true>(s, h, c, lim - kBlockKeys * blk, m, l, alpha, pb);
-        }
+        softmax(blk, s, alpha, pb);
         pv_accumulate<D, NT>(acc, 0, alpha, pb, sV + cur * C::kVStage, lane);
       }
       if constexpr (!SPLIT) {

@@ -24,8 +24,12 @@
  *     NULL is the null stream).  Calls on different streams may run concurrently.
  *   - Mask: key j of a sequence with L_q queries and L_k keys is visible from
  *     query row i iff j < L_k and (causal == 0 or j <= i + L_k - L_q), i.e.
- *     causal masks are aligned to the bottom-right corner.  A row with no
- *     visible key gets O = 0 and lse = -inf.
+ *     causal masks are aligned to the bottom-right corner.  A sliding window
+ *     (local attention; window-sized bounds of the aiter MQA-logits page)
+ *     window_left >= 0 further requires j >= i + L_k - L_q - window_left and
+ *     window_right >= 0 requires j <= i + L_k - L_q + window_right, on the same
+ *     diagonal; -1 leaves that side unbounded.  Keys outside a tile's window
+ *     are never read.  A row with no visible key gets O = 0 and lse = -inf.
  *   - Grouped-query attention: query head h reads kv head h / (Hq / Hkv).
  *   - dtype DA_BF16: Q, K, V are bf16, all descales must be 1.0f.
  *     dtype DA_FP8_E4M3: Q, K, V are OCP E4M3FN codes with per-tensor fp32
@@ -106,14 +110,16 @@ da_status attn_prefill_fwd(int32_t dtype, const void* q, const void* k, const vo
                            int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                            int64_t total_q, int64_t total_k, int32_t num_heads_q,
                            int32_t num_heads_kv, int32_t head_dim, float softmax_scale,
-                           int32_t causal, float q_descale, float k_descale, float v_descale,
+                           int32_t causal, int32_t window_left, int32_t window_right,
+                           float q_descale, float k_descale, float v_descale,
                            int32_t schedule, void* o, float* lse, float* partials,
                            size_t partials_bytes, void* stream);
 
 /*
  * Single-token decode over a paged KV cache: sequence b's query (row b of q) is
  * the last token of a sequence of context_lens[b] tokens, so every cached key
- * j < context_lens[b] is visible.  Token j of sequence b lives in page
+ * j < context_lens[b] is visible (j >= context_lens[b] - 1 - window_left as well
+ * when window_left >= 0; pages wholly below that are not read).  Token j of sequence b lives in page
  * page_table[b * max_pages_per_seq + j / 16] at slot j % 16.
  *   q         [batch, Hq, D]
  *   k_cache, v_cache  element (page, slot, kv_head, d) at
@@ -138,11 +144,11 @@ da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cach
                                 int64_t token_stride, int64_t head_stride,
                                 const int32_t* page_table, int32_t max_pages_per_seq,
                                 const int32_t* context_lens, int32_t max_context_len,
-                                int32_t batch, int32_t page_size, int32_t num_heads_q,
-                                int32_t num_heads_kv, int32_t head_dim, float softmax_scale,
-                                float q_descale, float k_descale, float v_descale,
-                                int32_t schedule, float* partials, size_t partials_bytes,
-                                void* o, float* lse, void* stream);
+                                int32_t window_left, int32_t batch, int32_t page_size,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                float softmax_scale, float q_descale, float k_descale,
+                                float v_descale, int32_t schedule, float* partials,
+                                size_t partials_bytes, void* o, float* lse, void* stream);
 
 /*
  * Prefix-cached extend over a paged KV cache, for a batch that mixes prefill,
@@ -169,9 +175,10 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
                                 const int32_t* context_lens, int32_t batch, int32_t max_seqlen_q,
                                 int32_t max_context_len, int64_t total_q, int32_t page_size,
                                 int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                                float softmax_scale, int32_t causal, float q_descale,
-                                float k_descale, float v_descale, int32_t schedule, void* o,
-                                float* lse, float* partials, size_t partials_bytes, void* stream);
+                                float softmax_scale, int32_t causal, int32_t window_left,
+                                int32_t window_right, float q_descale, float k_descale,
+                                float v_descale, int32_t schedule, void* o, float* lse,
+                                float* partials, size_t partials_bytes, void* stream);
 
 /*
  * Fold chunk partials into O: for every (row, head), partials c = 0 .. max_chunks-1

@@ -60,8 +60,8 @@ def test_small_helpers(lib):
 def _prefill_args(**over):
     a = dict(dtype=0, q=FAKE, k=FAKE, v=FAKE, cu_q=FAKE, cu_k=FAKE, batch=1, max_q=300,
              max_k=300, total_q=300, total_k=300, hq=2, hkv=1, d=64, scale=0.125, causal=1,
-             qd=1.0, kd=1.0, vd=1.0, schedule=0, o=FAKE, lse=None, part=None, part_bytes=0,
-             stream=None)
+             wl=-1, wr=-1, qd=1.0, kd=1.0, vd=1.0, schedule=0, o=FAKE, lse=None, part=None,
+             part_bytes=0, stream=None)
     a.update(over)
     return list(a.values())
 
@@ -85,6 +85,8 @@ def _prefill_args(**over):
     (dict(schedule=1, part=None), DA_EINVAL),
     (dict(schedule=1, part=FAKE, part_bytes=1024), DA_EWORKSPACE),
     (dict(max_q=1 << 30), DA_EUNSUPPORTED),  # beyond 32-bit descriptor offsets
+    (dict(wl=-2), DA_EINVAL),               # windows are >= 0 or -1 (unbounded)
+    (dict(wr=-5), DA_EINVAL),
 ])
 def test_prefill_validation(lib, over, status):
     assert lib.attn_prefill_fwd(*_prefill_args(**over)) == status
@@ -93,8 +95,8 @@ def test_prefill_validation(lib, over, status):
 def _decode_args(**over):
     a = dict(dtype=0, q=FAKE, kc=FAKE, vc=FAKE, num_pages=100, page_stride=16 * 8 * 128,
              token_stride=8 * 128, head_stride=128, table=FAKE, max_pages=64, ctx=FAKE,
-             max_ctx=1024, batch=4, page_size=16, hq=32, hkv=8, d=128, scale=0.088, qd=1.0,
-             kd=1.0, vd=1.0, schedule=1, part=FAKE, part_bytes=1 << 40, o=None, lse=None,
+             max_ctx=1024, wl=-1, batch=4, page_size=16, hq=32, hkv=8, d=128, scale=0.088,
+             qd=1.0, kd=1.0, vd=1.0, schedule=1, part=FAKE, part_bytes=1 << 40, o=None, lse=None,
              stream=None)
     a.update(over)
     return list(a.values())
@@ -113,6 +115,7 @@ def _decode_args(**over):
     (dict(schedule=0, o=None), DA_EINVAL),
     (dict(d=96), DA_EUNSUPPORTED),
     (dict(vd=2.0), DA_EINVAL),
+    (dict(wl=-3), DA_EINVAL),
 ])
 def test_decode_validation(lib, over, status):
     assert lib.attn_decode_split_fwd(*_decode_args(**over)) == status
@@ -122,8 +125,8 @@ def _extend_args(**over):
     a = dict(dtype=0, q=FAKE, cu_q=FAKE, kc=FAKE, vc=FAKE, num_pages=100,
              page_stride=16 * 8 * 128, token_stride=8 * 128, head_stride=128, table=FAKE,
              max_pages=64, ctx=FAKE, batch=4, max_q=300, max_ctx=1024, total_q=600,
-             page_size=16, hq=32, hkv=8, d=128, scale=0.088, causal=1, qd=1.0, kd=1.0, vd=1.0,
-             schedule=0, o=FAKE, lse=None, part=None, part_bytes=0, stream=None)
+             page_size=16, hq=32, hkv=8, d=128, scale=0.088, causal=1, wl=-1, wr=-1, qd=1.0,
+             kd=1.0, vd=1.0, schedule=0, o=FAKE, lse=None, part=None, part_bytes=0, stream=None)
     a.update(over)
     return list(a.values())
 
@@ -151,6 +154,7 @@ def _extend_args(**over):
     (dict(schedule=1, part=None), DA_EINVAL),
     (dict(schedule=1, part=FAKE, part_bytes=4096), DA_EWORKSPACE),
     (dict(max_q=1 << 28), DA_EUNSUPPORTED),   # beyond 32-bit descriptor offsets
+    (dict(wl=-7), DA_EINVAL),
     (dict(batch=0), DA_OK),                   # no work: nothing launched
 ])
 def test_paged_extend_validation(lib, over, status):
