@@ -112,9 +112,18 @@ __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x16 mfma_fp8(u32x2 a, u32x2 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(__builtin_bit_cast(long, a),
-                                                    __builtin_bit_cast(long, b), c, 0, 0, 0);
+// 32x32x64 fp8 x fp8 (OCP E4M3 operands, format code 0) with unit block
+// scales (E8M0 127 = 2^0): 64-wide K per instruction, twice the bf16 rate.
+// Lane l supplies row (A) / column (B) l % 32 and 32 K-values of half l / 32;
+// both operands use the same K slots, so the sum covers each K-value once.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma_fp8x64(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1,
+                                              f32x16 c) {
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                   (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                   (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x7f, 0, 0x7f);
 }
 
 }  // namespace detattn

@@ -10,8 +10,9 @@
 //   * keys are consumed in 64-key blocks at absolute positions inside 512-key
 //     chunks; each chunk's online softmax starts from the empty state
 //     (m = -inf, l = 0, acc = 0);
-//   * S^T = K Q^T per block on v_mfma_f32_32x32x16 (bf16, or fp8 for e4m3
-//     inputs), D/16 K-steps in ascending order from a zero accumulator; the
+//   * S^T = K Q^T per block on v_mfma_f32_32x32x16_bf16 with D/16 K-steps, or
+//     for e4m3 inputs on v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales) with
+//     D/64 K-steps, in ascending order from a zero accumulator; the
 //     instruction shape and the K order are part of the contract, as the same
 //     page says of its GEMM sibling (section 1);
 //   * scores are masked by select (to -inf), never by adding; the block max is
@@ -50,13 +51,13 @@ struct Geom {
   static constexpr int kEs = FP8 ? 1 : 2;       // bytes per Q/K/V element in HBM
   static constexpr int kRowBytes = D * kEs;     // one head row of Q/K/V
   // LDS row strides, chosen for gfx950's 64 four-byte banks (256 bytes per
-  // cycle).  K rows are read 16 bytes (bf16) or 8 bytes (fp8) per lane, 16 or
-  // 32 lanes per cycle, one row per lane: an odd number of access units per
-  // row puts those rows on distinct banks.  V rows are read by the transposing
+  // cycle).  K rows are read 16 bytes per lane and instruction, 16 lanes per
+  // cycle, one row per lane: an odd number of 16-byte units per row puts those
+  // rows on distinct banks (and keeps the reads 16-byte aligned).  V rows are read by the transposing
   // read, four rows x 64 bytes per 32-lane cycle: a stride of 64 mod 256 bytes
   // puts the four rows on disjoint banks.
   static constexpr int kQRow = kRowBytes + 16;
-  static constexpr int kKRow = kRowBytes + (FP8 ? 8 : 16);
+  static constexpr int kKRow = kRowBytes + 16;
   static constexpr int kVRow = D * 2 + 64;      // V is staged as bf16
   static constexpr int kKStage = kBlockKeys * kKRow;
   static constexpr int kVStage = kBlockKeys * kVRow;
@@ -93,15 +94,27 @@ __device__ __forceinline__ void qk_scores_qrow(f32x16 (&s)[2], const unsigned ch
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+  if constexpr (FP8) {
+    // e4m3: D/64 K-steps of 64 on the 32x32x64 instruction, each lane reading
+    // the 32 bytes of its half of the step from its K row and its Q row.
+    static_assert(D % 64 == 0, "fp8 head_dim must be a multiple of 64");
 #pragma unroll
-  for (int st = 0; st < G::kSteps; ++st) {
-    const uint32_t qoff = (uint32_t)((16 * st + 8 * h) * G::kEs);
+    for (int st = 0; st < D / 64; ++st) {
+      const uint32_t qoff = (uint32_t)(64 * st + 32 * h);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t off = (uint32_t)(krow + 2 * t * KPAGE + (16 * st + 8 * h) * G::kEs);
-      if constexpr (FP8) {
-        s[t] = mfma_fp8(lds_load8(ks, off), lds_load8(qrow, qoff), s[t]);
-      } else {
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t off = (uint32_t)(krow + 2 * t * KPAGE + 64 * st + 32 * h);
+        s[t] = mfma_fp8x64(lds_load16(ks, off), lds_load16(ks, off + 16), lds_load16(qrow, qoff),
+                           lds_load16(qrow, qoff + 16), s[t]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) {
+      const uint32_t qoff = (uint32_t)((16 * st + 8 * h) * G::kEs);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t off = (uint32_t)(krow + 2 * t * KPAGE + (16 * st + 8 * h) * G::kEs);
         s[t] = mfma_bf16(lds_load16(ks, off), lds_load16(qrow, qoff), s[t]);
       }
     }
