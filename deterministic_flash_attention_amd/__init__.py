@@ -2,10 +2,12 @@
 
 The functions named like the C entry points (``attn_prefill_fwd``,
 ``attn_decode_split_fwd``, ``attn_paged_extend_fwd``, ``attn_chunk_merge``,
-``attn_partials_bytes``, ``attn_num_chunks``, ``attn_status_str``) take torch
+``attn_partials_bytes``, ``attn_num_chunks``, ``attn_status_str``, and the GEMM's
+``det_gemm_fwd``, ``det_gemm_workspace_bytes``, ``det_gemm_num_chunks``,
+``det_gemm_num_configs``, ``det_gemm_config_tile``) take torch
 tensors that already live on the GPU, pass their device pointers and sizes to
 the C ABI and raise ``DetAttnError`` on a non-zero status.  ``prefill``,
-``decode`` and ``paged_extend`` additionally
+``decode``, ``paged_extend`` and ``gemm`` additionally
 allocate the outputs (and the partials of the split schedule) with torch and
 chain the split and merge launches on the current stream.  Every step of the
 computation runs in the HIP kernels of the library; there is no fallback: if the
@@ -24,12 +26,16 @@ __all__ = [
     "DetAttnError", "BF16", "FP8_E4M3", "MONOLITHIC", "SPLIT", "BLOCK_KEYS", "CHUNK_KEYS",
     "PAGE_SIZE", "library_path", "load_library", "attn_status_str", "attn_num_chunks",
     "attn_partials_bytes", "attn_prefill_fwd", "attn_decode_split_fwd", "attn_paged_extend_fwd",
-    "attn_chunk_merge", "prefill", "decode", "paged_extend",
+    "attn_chunk_merge", "prefill", "decode", "paged_extend", "WEIGHT_NK", "WEIGHT_KN",
+    "GEMM_BLOCK_K", "GEMM_CHUNK_K", "det_gemm_num_chunks", "det_gemm_workspace_bytes",
+    "det_gemm_num_configs", "det_gemm_config_tile", "det_gemm_fwd", "gemm",
 ]
 
 BF16, FP8_E4M3 = 0, 1
 MONOLITHIC, SPLIT = 0, 1
 BLOCK_KEYS, CHUNK_KEYS, PAGE_SIZE = 64, 512, 16
+WEIGHT_NK, WEIGHT_KN = 0, 1
+GEMM_BLOCK_K, GEMM_CHUNK_K = 64, 1024
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB: Optional[ctypes.CDLL] = None
@@ -79,6 +85,17 @@ def load_library() -> ctypes.CDLL:
     lib.attn_paged_extend_fwd.restype = ctypes.c_int
     lib.attn_chunk_merge.argtypes = [c_p, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p]
     lib.attn_chunk_merge.restype = ctypes.c_int
+    lib.det_gemm_num_chunks.argtypes = [c_i64]
+    lib.det_gemm_num_chunks.restype = c_i32
+    lib.det_gemm_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
+    lib.det_gemm_workspace_bytes.restype = c_sz
+    lib.det_gemm_num_configs.argtypes = []
+    lib.det_gemm_num_configs.restype = c_i32
+    lib.det_gemm_config_tile.argtypes = [c_i32, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32)]
+    lib.det_gemm_config_tile.restype = ctypes.c_int
+    lib.det_gemm_fwd.argtypes = [c_p, c_i64, c_p, c_i64, c_i32, c_p, c_i64, c_i64, c_i64, c_i64,
+                                 c_i32, c_i32, c_p, c_sz, c_p]
+    lib.det_gemm_fwd.restype = ctypes.c_int
     _LIB = lib
     return lib
 
@@ -192,7 +209,69 @@ def attn_chunk_merge(partials, rows: int, num_heads_q: int, max_chunks: int, hea
     _check("attn_chunk_merge", st)
 
 
+def _rows_ptr(t: Optional[torch.Tensor]) -> Tuple[Optional[int], int]:
+    """Pointer and row stride (elements) of a 2-D tensor with unit column stride."""
+    if t is None:
+        return None, 0
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("GEMM operands must be 2-D with contiguous rows")
+    return t.data_ptr(), int(t.stride(0)) if t.shape[0] > 1 else int(max(t.stride(0), t.shape[1]))
+
+
+def det_gemm_num_chunks(k: int) -> int:
+    return int(load_library().det_gemm_num_chunks(int(k)))
+
+
+def det_gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(load_library().det_gemm_workspace_bytes(int(m), int(n), int(k)))
+
+
+def det_gemm_num_configs() -> int:
+    return int(load_library().det_gemm_num_configs())
+
+
+def det_gemm_config_tile(config: int) -> Tuple[int, int]:
+    bm, bn = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("det_gemm_config_tile",
+           load_library().det_gemm_config_tile(int(config), ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def det_gemm_fwd(a, w, c, weight_layout: int = WEIGHT_NK, schedule: int = MONOLITHIC,
+                 config: int = -1, workspace=None, stream=None) -> None:
+    """Mirror of the C ``det_gemm_fwd``: C = A W^T (W [N, K]) or A W (W [K, N]).
+    Row strides are taken from the tensors (rows must be contiguous)."""
+    m, k = a.shape
+    n = w.shape[0] if weight_layout == WEIGHT_NK else w.shape[1]
+    if c.shape[0] != m or c.shape[1] != n:
+        raise ValueError("C must be [M, N]")
+    pa, lda = _rows_ptr(a)
+    pw, ldw = _rows_ptr(w)
+    pc, ldc = _rows_ptr(c)
+    st = load_library().det_gemm_fwd(
+        pa, lda, pw, ldw, int(weight_layout), pc, ldc, int(m), int(n), int(k), int(schedule),
+        int(config), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("det_gemm_fwd", st)
+
+
 # ------------------------------------------------------------- conveniences
+def gemm(a, w, weight_layout: int = WEIGHT_NK, schedule: Optional[int] = None, config: int = -1,
+         out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+         stream=None) -> torch.Tensor:
+    """Batch-invariant C = A W^T ([N, K] weight) or A W ([K, N] weight) in bf16.
+    schedule None picks SPLIT when M is at most 64 (decode-sized), else
+    MONOLITHIC; both give the same bits."""
+    m = a.shape[0]
+    n = w.shape[0] if weight_layout == WEIGHT_NK else w.shape[1]
+    if schedule is None:
+        schedule = SPLIT if m <= 64 else MONOLITHIC
+    c = out if out is not None else torch.empty(m, n, dtype=torch.bfloat16, device=a.device)
+    if schedule == SPLIT and workspace is None:
+        nbytes = det_gemm_workspace_bytes(m, n, a.shape[1])
+        workspace = torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=a.device)
+    det_gemm_fwd(a, w, c, weight_layout, schedule, config, workspace, stream)
+    return c
 def _new_partials(rows: int, hq: int, cmax: int, d: int, device) -> torch.Tensor:
     nbytes = attn_partials_bytes(rows, hq, cmax, d)
     return torch.empty(max(nbytes // 4, 4), dtype=torch.float32, device=device)

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdetattn.so")
-SOURCES = ["abi.cpp", "prefill.hip", "decode.hip", "merge.hip"]
+SOURCES = ["abi.cpp", "prefill.hip", "decode.hip", "merge.hip", "gemm.hip"]
 
 # -ffp-contract=off: the compiler fuses no multiply-add (part of the numerical contract).
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU instructions.

@@ -8,6 +8,7 @@
 #include <limits>
 
 #include "../../include/detattn.h"
+#include "../../include/detgemm.h"
 #include "kernels.hpp"
 
 namespace {
@@ -36,6 +37,27 @@ size_t partials_bytes_or_max(int64_t rows, int64_t hq, int64_t chunks, int64_t d
   const long double n = (long double)rows * hq * chunks * (d + 2) * 4.0L;
   if (n > (long double)std::numeric_limits<size_t>::max() / 2) return std::numeric_limits<size_t>::max();
   return (size_t)rows * (size_t)hq * (size_t)chunks * (size_t)(d + 2) * 4u;
+}
+
+int32_t gemm_chunks(int64_t k) { return k <= 0 ? 0 : (int32_t)((k + DG_CHUNK_K - 1) / DG_CHUNK_K); }
+
+// Tile shape when the caller leaves it open: the largest tile whose launch
+// (tiles x split factor) still covers the 256 compute units, else the one with
+// the most workgroups.  Every choice computes the same bits.
+int32_t gemm_auto_config(int64_t m, int64_t n, int64_t split_factor) {
+  int32_t best = 0;
+  int64_t best_count = -1;
+  for (int32_t cfg = 0; cfg < detattn::gemm_num_configs(); ++cfg) {
+    int bm = 0, bn = 0;
+    detattn::gemm_config_tile(cfg, &bm, &bn);
+    const int64_t count = ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * split_factor;
+    if (count >= 256) return cfg;
+    if (count > best_count) {
+      best = cfg;
+      best_count = count;
+    }
+  }
+  return best;
 }
 
 }  // namespace
@@ -295,6 +317,82 @@ da_status attn_chunk_merge(const float* partials, size_t partials_bytes, int64_t
   p.cmax = max_chunks;
   p.v_descale = v_descale;
   const hipError_t e = detattn::launch_merge(p, head_dim, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ELAUNCH;
+}
+
+// ---- batch-invariant GEMM ------------------------------------------------------
+
+int32_t det_gemm_num_chunks(int64_t k) { return gemm_chunks(k); }
+
+size_t det_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k < 0) return 0;
+  const long double b = (long double)gemm_chunks(k) * m * n * 4.0L;
+  if (b > (long double)std::numeric_limits<size_t>::max() / 2) return std::numeric_limits<size_t>::max();
+  return (size_t)gemm_chunks(k) * (size_t)m * (size_t)n * 4u;
+}
+
+int32_t det_gemm_num_configs(void) { return detattn::gemm_num_configs(); }
+
+da_status det_gemm_config_tile(int32_t config, int32_t* bm, int32_t* bn) {
+  if (config < 0 || config >= detattn::gemm_num_configs() || !bm || !bn) return DA_EINVAL;
+  int m = 0, n = 0;
+  detattn::gemm_config_tile(config, &m, &n);
+  *bm = m;
+  *bn = n;
+  return DA_OK;
+}
+
+da_status det_gemm_fwd(const void* a, int64_t lda, const void* w, int64_t ldw,
+                       int32_t weight_layout, void* c, int64_t ldc, int64_t m, int64_t n,
+                       int64_t k, int32_t schedule, int32_t config, float* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (weight_layout != DG_WEIGHT_NK && weight_layout != DG_WEIGHT_KN) return DA_EINVAL;
+  if (schedule != DA_MONOLITHIC && schedule != DA_SPLIT) return DA_EINVAL;
+  if (m < 0 || n < 0 || k < 0) return DA_EINVAL;
+  if (config < -1 || config >= detattn::gemm_num_configs()) return DA_EINVAL;
+  if (n % 8 || k % 8) return DA_EUNSUPPORTED;
+  const bool kn = weight_layout == DG_WEIGHT_KN;
+  const bool split = schedule == DA_SPLIT;
+  if (m == 0 || n == 0) return DA_OK;
+  if (!c || !aligned(c, 16) || ldc < n || ldc % 8) return DA_EINVAL;
+  if (k > 0) {
+    if (!a || !aligned(a, 16) || lda < k || lda % 8) return DA_EINVAL;
+    if (!w || !aligned(w, 16) || ldw < (kn ? n : k) || ldw % 8) return DA_EINVAL;
+  }
+  const int32_t nchunks = gemm_chunks(k);
+  if (split && nchunks > 0) {
+    if (!workspace || !aligned(workspace, 16)) return DA_EINVAL;
+    if (workspace_bytes < det_gemm_workspace_bytes(m, n, k)) return DA_EWORKSPACE;
+  }
+  if (config < 0) config = gemm_auto_config(m, n, split ? nchunks : 1);
+  int32_t bm = 0, bn = 0;
+  det_gemm_config_tile(config, &bm, &bn);
+  // Every byte offset inside one tile's descriptor must stay below 2^31.
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
+  if (tiles > kMaxOffset || m * (n / 4) / 256 > kMaxOffset) return DA_EUNSUPPORTED;
+  if (k > 0) {
+    if (((bm - 1) * lda + k) * 2 > kMaxOffset) return DA_EUNSUPPORTED;
+    if (kn ? (k * ldw + bn) * 2 > kMaxOffset : ((bn - 1) * ldw + k) * 2 > kMaxOffset)
+      return DA_EUNSUPPORTED;
+  }
+  if (((bm - 1) * ldc + bn) * 2 > kMaxOffset) return DA_EUNSUPPORTED;
+  if (split && ((bm - 1) * n + bn) * 4 > kMaxOffset) return DA_EUNSUPPORTED;
+
+  detattn::GemmParams p{};
+  p.a = a;
+  p.b = w;
+  p.c = c;
+  p.part = workspace;
+  p.lda = lda;
+  p.ldb = ldw;
+  p.ldc = ldc;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  p.nchunks = nchunks;
+  p.group_m = 8;
+  const hipError_t e =
+      detattn::launch_gemm(p, config, kn, split, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ELAUNCH;
 }
 

@@ -1,0 +1,444 @@
+// Batch-invariant bf16 GEMM on gfx950 (RL-Kernel PR "MFMA batch-invariant GEMM
+// and chunked Triton attention", section 1).
+//
+// C[M, N] = A[M, K] B[K, N], B = W^T for an [N, K] weight or W itself for a
+// [K, N] weight.  The numerical contract, identical for every configuration:
+//   - every product runs on v_mfma_f32_32x32x16_bf16 (the pinned MFMA shape);
+//     MFMA step s of K block b covers K indices 64 b + 16 s + [0, 16), lane half
+//     h supplying K offsets 8 h + [0, 8) for both operands;
+//   - K is consumed in ascending 64-wide blocks; the partial of each 1024-wide
+//     chunk starts from +0 and chains its blocks' MFMAs in order;
+//   - chunk partials are added left to right in fp32 (total = p_0, then
+//     total = total + p_c), and the total is rounded once to bf16 (nearest even).
+// Every output element depends only on its row of A and its column of B, so the
+// tile shape, the wave count, the stage count, the weight layout, M, the row
+// stride and the schedule give the same bits.  The split schedule runs one
+// workgroup per (tile, chunk), stores fp32 chunk partials and folds them in the
+// same left-to-right order in gemm_combine_kernel.
+//
+// Data movement: each 64-wide K block of the A tile and the B tile is copied
+// global -> LDS with direct (buffer_load ... lds) loads, STAGES blocks in flight.
+// A and [N, K] B tiles keep 128-byte rows whose 16-byte chunks are XOR-swizzled
+// by (row / 2) % 8, so 16 consecutive rows read at one K offset hit 16 distinct
+// bank groups; a [K, N] B tile keeps 64 K rows padded by 64 bytes and is read
+// with the transposing LDS read.  Out-of-range rows, columns past a [K, N] row
+// end and K past the end read as zero through the buffer range check.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace detattn {
+
+namespace {
+
+constexpr int kGemmBlockK = 64;       // K per block
+constexpr int kGemmBlocksPerChunk = 16;  // 1024 / 64
+constexpr uint32_t kParkedOff = 0x80000000u;  // past every descriptor (offsets stay below 2^31)
+
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool KN>
+struct GemmCfg {
+  static constexpr int kNW = WM * WN;
+  static constexpr int kThreads = kNW * 64;
+  static constexpr int kTM = BM / WM, kTN = BN / WN;  // wave tile
+  static constexpr int kSM = kTM / 32, kSN = kTN / 32;
+  static_assert(kTM % 32 == 0 && kTN % 32 == 0, "wave tiles are whole 32x32 MFMA tiles");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 blocks in flight");
+  // A stage: BM rows of 128 bytes; loads per wave rounded up so every wave
+  // issues the same count (the surplus lanes write zeros into the stage's tail).
+  static constexpr int kAPer = cdiv(BM * 128, 1024 * kNW);
+  static constexpr int kAStage = kAPer * kNW * 1024;
+  static constexpr int kBRow = KN ? BN * 2 + 64 : 128;
+  static constexpr int kBSlots = kBRow / 16;
+  static constexpr int kBRows = KN ? kGemmBlockK : BN;
+  static constexpr int kBPer = cdiv(kBRows * kBRow, 1024 * kNW);
+  static constexpr int kBStage = kBPer * kNW * 1024;
+  static constexpr int kStage = kAStage + kBStage;
+  // as many of the requested stages as fit in the 160 KB of LDS
+  static constexpr int kStages = STAGES * kStage <= 160 * 1024 ? STAGES : 160 * 1024 / kStage;
+  static_assert(kStages >= 2, "two stages must fit");
+  static constexpr int kLds = kStages * kStage;
+  static constexpr int kPer = kAPer + kBPer;  // direct loads per wave per block
+  // Eight waves as two groups of four (4 x 2 wave grid) with three stages run
+  // the ping-pong schedule; the rest run all waves in lockstep.
+  static constexpr bool kPingPong = kNW == 8 && WM == 4 && kStages == 3;
+};
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the implicit memory fence of __syncthreads(): the
+// direct loads still in flight are not waited for (wait_vm_le does that for the
+// block being published); the asm statements keep LDS accesses on their side.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool KN, bool SPLIT>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmParams p) {
+  using C = GemmCfg<BM, BN, WM, WN, STAGES, KN>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::kLds];
+
+  // ---- tile of this workgroup -------------------------------------------
+  // Consecutive workgroup ids go round-robin to the 8 XCDs; give each XCD a
+  // contiguous range of tiles, ordered group_m tile rows at a time (column by
+  // column inside a group), so the tiles resident on one XCD share A rows and
+  // B columns in its L2.
+  const int T = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int q8 = T / 8, r8 = T % 8, x = bid % 8, ix = bid / 8;
+  const int t = x < r8 ? x * (q8 + 1) + ix : r8 * (q8 + 1) + (x - r8) * q8 + ix;
+  const int per_group = p.group_m * p.tiles_n;
+  const int g = t / per_group, tg = t % per_group;
+  const int first_m = g * p.group_m;
+  const int rows_in_group = min(p.group_m, p.tiles_m - first_m);
+  const int tm = first_m + tg % rows_in_group, tn = tg / rows_in_group;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int rows_a = (int)min((int64_t)BM, p.m - m0);
+  const int cols_b = (int)min((int64_t)BN, p.n - n0);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave % WM, wn = wave / WM;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // ---- descriptors: one per operand tile, bounded to its valid cells -------
+  const int64_t K = p.k;
+  const rsrc_t ra = make_rsrc(static_cast<const unsigned char*>(p.a) + m0 * p.lda * 2,
+                              (uint32_t)(((int64_t)(rows_a - 1) * p.lda + K) * 2));
+  const rsrc_t rb =
+      KN ? make_rsrc(static_cast<const unsigned char*>(p.b) + n0 * 2,
+                     (uint32_t)(((K - 1) * p.ldb + cols_b) * 2))
+         : make_rsrc(static_cast<const unsigned char*>(p.b) + n0 * p.ldb * 2,
+                     (uint32_t)(((int64_t)(cols_b - 1) * p.ldb + K) * 2));
+
+  // ---- per-lane direct-load slots -----------------------------------------
+  // A (and [N, K] B): LDS position pos = 1024 seg + 16 lane holds row pos / 128,
+  // K chunk (pos / 16 % 8) ^ (row / 2 % 8).  kidx is the slot's first K index
+  // inside a block (huge for surplus slots, so they always read as zero).
+  uint32_t aoff[C::kAPer], boff[C::kBPer];
+  int akidx[C::kAPer], bkidx[C::kBPer];
+#pragma unroll
+  for (int u = 0; u < C::kAPer; ++u) {
+    const int pos = 64 * (wave + C::kNW * u) + lane, r = pos >> 3;
+    const int c = (pos & 7) ^ ((r >> 1) & 7);
+    const bool ok = r < BM;
+    aoff[u] = ok ? (uint32_t)(r * p.lda * 2 + 16 * c) : kParkedOff;
+    akidx[u] = ok ? 8 * c : (1 << 30);
+  }
+#pragma unroll
+  for (int u = 0; u < C::kBPer; ++u) {
+    const int pos = 64 * (wave + C::kNW * u) + lane;
+    if constexpr (KN) {
+      const int r = pos / C::kBSlots, c = pos % C::kBSlots;
+      const bool ok = r < kGemmBlockK && c < BN / 8;
+      boff[u] = ok ? (uint32_t)(r * p.ldb * 2 + 16 * c) : kParkedOff;
+      bkidx[u] = ok ? r : (1 << 30);
+    } else {
+      const int r = pos >> 3, c = (pos & 7) ^ ((r >> 1) & 7);
+      const bool ok = r < BN;
+      boff[u] = ok ? (uint32_t)(r * p.ldb * 2 + 16 * c) : kParkedOff;
+      bkidx[u] = ok ? 8 * c : (1 << 30);
+    }
+  }
+  const uint32_t b_kstride = KN ? (uint32_t)(p.ldb * 2) : 2u;  // bytes per K index
+
+  auto issue = [&](int blk, int st) {
+    const int k0 = blk * kGemmBlockK;
+    unsigned char* sa = smem + st * C::kStage;
+    unsigned char* sb = sa + C::kAStage;
+#pragma unroll
+    for (int u = 0; u < C::kAPer; ++u) {
+      const uint32_t off = (int64_t)(k0 + akidx[u]) < K ? aoff[u] + 2u * (uint32_t)k0 : kParkedOff;
+      buf_load16_lds(ra, sa + (wave + C::kNW * u) * 1024, off);
+    }
+#pragma unroll
+    for (int u = 0; u < C::kBPer; ++u) {
+      const uint32_t off =
+          (int64_t)(k0 + bkidx[u]) < K ? boff[u] + b_kstride * (uint32_t)k0 : kParkedOff;
+      buf_load16_lds(rb, sb + (wave + C::kNW * u) * 1024, off);
+    }
+  };
+
+  // ---- LDS read offsets -----------------------------------------------------
+  // Row r = (32-aligned base) + l32 at K chunk 2 s + h sits at chunk slot
+  // (2 s + h) ^ (l32 / 2 % 8).
+  uint32_t coff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) coff[s] = 16u * (uint32_t)((2 * s + h) ^ ((l32 >> 1) & 7));
+  const uint32_t a_row = (uint32_t)((wm * C::kTM + l32) * 128);
+  const uint32_t b_row = (uint32_t)((wn * C::kTN + l32) * 128);
+  // [K, N] B through the transposing read: lane (group grp, li) addresses row
+  // 16 s + 8 h + li / 4 (and 4 rows on), column base + 16 (grp % 2) + 4 (li % 4).
+  const int grp = lane >> 4, li = lane & 15;
+  const uint32_t b_tr = (uint32_t)((8 * h + (li >> 2)) * C::kBRow +
+                                   (wn * C::kTN + 16 * (grp & 1) + 4 * (li & 3)) * 2);
+
+  f32x16 acc[C::kSM][C::kSN];
+  f32x16 tot[C::kSM][C::kSN];
+#pragma unroll
+  for (int i = 0; i < C::kSM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::kSN; ++j) {
+      acc[i][j] = f32x16{};
+      tot[i][j] = f32x16{};
+    }
+
+  // Operands of MFMA step s from stage st: A tiles i, B tiles j of this wave.
+  auto read_a = [&](int st, int s, int i) -> u32x4 {
+    return lds_load16(smem + st * C::kStage, a_row + 32u * 128u * i + coff[s]);
+  };
+  auto read_b = [&](int st, int s, int j) -> u32x4 {
+    const unsigned char* sb = smem + st * C::kStage + C::kAStage;
+    if constexpr (KN) {
+      const uint32_t off = b_tr + (uint32_t)(16 * s * C::kBRow + 64 * j);
+      const u32x2 lo = __builtin_bit_cast(u32x2, lds_load_tr16(sb, off));
+      const u32x2 hi = __builtin_bit_cast(u32x2, lds_load_tr16(sb, off + 4 * C::kBRow));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+      return lds_load16(sb, b_row + 32u * 128u * j + coff[s]);
+    }
+  };
+  // One block, step by step: read a step's operands, run its MFMAs.
+  auto compute = [&](int st) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 a[C::kSM], b[C::kSN];
+#pragma unroll
+      for (int i = 0; i < C::kSM; ++i) a[i] = read_a(st, s, i);
+#pragma unroll
+      for (int j = 0; j < C::kSN; ++j) b[j] = read_b(st, s, j);
+#pragma unroll
+      for (int i = 0; i < C::kSM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::kSN; ++j) acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
+    }
+  };
+  // Chunk end: total = p_0, then total = total + p_c; the partial restarts at +0.
+  auto fold = [&](int blk, bool last) {
+    if (blk % kGemmBlocksPerChunk == kGemmBlocksPerChunk - 1 || last) {
+      if constexpr (!SPLIT) {
+        const bool first = blk < kGemmBlocksPerChunk;
+#pragma unroll
+        for (int i = 0; i < C::kSM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < C::kSN; ++jj) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              tot[i][jj][e] = first ? acc[i][jj][e] : tot[i][jj][e] + acc[i][jj][e];
+            acc[i][jj] = f32x16{};
+          }
+      }
+    }
+  };
+
+  // ---- K loop -----------------------------------------------------------------
+  const int nchunks = p.nchunks;
+  const int c_begin = SPLIT ? (int)blockIdx.y : 0;
+  const int c_end = SPLIT ? c_begin + 1 : nchunks;
+  const int nblocks_k = (int)((K + kGemmBlockK - 1) / kGemmBlockK);
+  const int blk_begin = c_begin * kGemmBlocksPerChunk;
+  const int blk_end = min(c_end * kGemmBlocksPerChunk, nblocks_k);
+  const int n = blk_end - blk_begin;
+
+  if constexpr (C::kPingPong) {
+    // Two groups of four waves, one per half of the tile's columns; wave w and
+    // wave w + 4 share a SIMD.  Group 1 runs one interval behind group 0, and
+    // every interval ends at a workgroup barrier, so on each SIMD one wave runs
+    // the 16 MFMAs of a block from registers while the other reads the next
+    // block's operands from LDS into registers and issues its share of the
+    // direct loads for the block two ahead.
+    //   interval 2j:   group 0 reads block j,  group 1 multiplies block j - 1
+    //   interval 2j+1: group 0 multiplies j,   group 1 reads block j
+    // Stage j is read in intervals 2j and 2j + 1 and refilled (block j + 3)
+    // from interval 2j + 2 on; before the barrier that opens interval 2j every
+    // wave has waited for its own loads of block j.
+    const int grp_id = wave >> 2;
+    u32x4 fa[4][C::kSM], fb[4][C::kSN];
+    if (n > 0) issue(blk_begin, 0);
+    if (n > 1) issue(blk_begin + 1, 1);
+    if (n > 1) wait_vm_le<C::kPer>();
+    else wait_vm_le<0>();
+    barrier();
+    for (int t = 0; t <= 2 * n; ++t) {
+      const int my = t - grp_id;
+      if (my >= 0 && my < 2 * n) {
+        const int j = my >> 1;
+        if ((my & 1) == 0) {
+          const int st = j % 3;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int i = 0; i < C::kSM; ++i) fa[s][i] = read_a(st, s, i);
+#pragma unroll
+            for (int jj = 0; jj < C::kSN; ++jj) fb[s][jj] = read_b(st, s, jj);
+          }
+          if (j + 2 < n) issue(blk_begin + j + 2, (j + 2) % 3);
+        } else {
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < C::kSM; ++i)
+#pragma unroll
+              for (int jj = 0; jj < C::kSN; ++jj)
+                acc[i][jj] = mfma_bf16(fa[s][i], fb[s][jj], acc[i][jj]);
+          __builtin_amdgcn_s_setprio(0);
+          fold(blk_begin + j, j == n - 1);
+        }
+      }
+      if (t & 1) {
+        // publish block (t + 1) / 2 for the interval that opens next
+        const int jn = (t + 1) >> 1;
+        if (jn < n) {
+          if (jn + 1 < n) wait_vm_le<C::kPer>();
+          else wait_vm_le<0>();
+        }
+      }
+      barrier();
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < C::kStages - 1; ++s)
+      if (s < n) issue(blk_begin + s, s);
+    for (int j = 0; j < n; ++j) {
+      // Block j is published once every wave has its loads: at most the loads
+      // of the blocks issued after it may still be in flight.
+      const int ahead = min(C::kStages - 2, n - 1 - j);
+      if constexpr (C::kStages >= 4) {
+        if (ahead >= 2) wait_vm_le<2 * C::kPer>();
+        else if (ahead == 1) wait_vm_le<C::kPer>();
+        else wait_vm_le<0>();
+      } else if constexpr (C::kStages == 3) {
+        if (ahead >= 1) wait_vm_le<C::kPer>();
+        else wait_vm_le<0>();
+      } else {
+        wait_vm_le<0>();
+      }
+      barrier();
+      if (j + C::kStages - 1 < n)
+        issue(blk_begin + j + C::kStages - 1, (j + C::kStages - 1) % C::kStages);
+      compute(j % C::kStages);
+      fold(blk_begin + j, j == n - 1);
+    }
+  }
+
+  // ---- epilogue ---------------------------------------------------------------
+  // Descriptors start at the tile's first cell (m0, n0).  Lane (l32, h) of
+  // output tile (i, j) holds column 32 j + l32 and rows
+  // 32 i + 8 (e / 4) + 4 h + e % 4 of its wave tile in element e.
+  if constexpr (SPLIT) {
+    const int64_t ld = p.n;
+    const rsrc_t rp = make_rsrc(p.part + ((int64_t)c_begin * p.m + m0) * ld + n0,
+                                (uint32_t)(((int64_t)(rows_a - 1) * ld + cols_b) * 4));
+#pragma unroll
+    for (int i = 0; i < C::kSM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kSN; ++j) {
+        const int col = wn * C::kTN + 32 * j + l32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = wm * C::kTM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+          const uint32_t off = col < cols_b ? (uint32_t)((row * ld + col) * 4) : kParkedOff;
+          buf_store4(rp, off, f32_bits(acc[i][j][e]));
+        }
+      }
+  } else {
+    const int64_t ld = p.ldc;
+    const rsrc_t rc = make_rsrc(static_cast<unsigned char*>(p.c) + (m0 * ld + n0) * 2,
+                                (uint32_t)(((int64_t)(rows_a - 1) * ld + cols_b) * 2));
+#pragma unroll
+    for (int i = 0; i < C::kSM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::kSN; ++j) {
+        const int col = wn * C::kTN + 32 * j + l32;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = wm * C::kTM + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+          const uint32_t off = col < cols_b ? (uint32_t)((row * ld + col) * 2) : kParkedOff;
+          buf_store2(rc, off, bf16_bits(tot[i][j][e]));
+        }
+      }
+  }
+}
+
+// Split schedule, second pass: C = bf16(((p_0 + p_1) + p_2) + ...), the same
+// left fold the monolithic kernel runs in registers.  One thread per 4
+// consecutive columns.
+__global__ __launch_bounds__(256) void gemm_combine_kernel(const GemmParams p) {
+  const int64_t quads = p.m * (p.n / 4);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= quads) return;
+  const int64_t row = idx / (p.n / 4), col = 4 * (idx % (p.n / 4));
+  const int64_t plane = p.m * p.n;
+  const float* src = p.part + row * p.n + col;
+  f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (p.nchunks > 0) t = *reinterpret_cast<const f32x4*>(src);
+  for (int c = 1; c < p.nchunks; ++c) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + c * plane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = t[e] + v[e];
+  }
+  u32x2 o;
+  o[0] = pack_bf16x2(t[0], t[1]);
+  o[1] = pack_bf16x2(t[2], t[3]);
+  *reinterpret_cast<u32x2*>(static_cast<unsigned char*>(p.c) + (row * p.ldc + col) * 2) = o;
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+hipError_t launch_cfg(const GemmParams& p0, bool kn, bool split, hipStream_t stream) {
+  GemmParams p = p0;
+  p.tiles_m = (int32_t)((p.m + BM - 1) / BM);
+  p.tiles_n = (int32_t)((p.n + BN - 1) / BN);
+  p.group_m = max(1, min(p.group_m, p.tiles_m));
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n), split ? (unsigned)p.nchunks : 1u);
+  const dim3 block(WM * WN * 64);
+  if (kn) {
+    if (split) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, true, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, true, false>), grid, block, 0, stream, p);
+  } else {
+    if (split) hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, STAGES, false, false>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_num_configs() { return 5; }
+
+void gemm_config_tile(int config, int* bm, int* bn) {
+  static const int kTiles[5][2] = {{256, 128}, {128, 128}, {64, 64}, {32, 64}, {32, 32}};
+  *bm = kTiles[config][0];
+  *bn = kTiles[config][1];
+}
+
+hipError_t launch_gemm(const GemmParams& p, int config, bool kn, bool split, hipStream_t stream) {
+  if (p.m > 0 && p.n > 0 && p.nchunks > 0) {
+    hipError_t e = hipSuccess;
+    switch (config) {
+      case 0: e = launch_cfg<256, 128, 4, 2, 3>(p, kn, split, stream); break;
+      case 1: e = launch_cfg<128, 128, 2, 2, 3>(p, kn, split, stream); break;
+      case 2: e = launch_cfg<64, 64, 2, 2, 4>(p, kn, split, stream); break;
+      case 3: e = launch_cfg<32, 64, 1, 2, 4>(p, kn, split, stream); break;
+      case 4: e = launch_cfg<32, 32, 1, 1, 4>(p, kn, split, stream); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess || !split) return e;
+  }
+  // Split combine; also the whole job when K = 0 (C = +0).
+  if (p.m > 0 && p.n > 0 && (split || p.nchunks == 0)) {
+    const int64_t quads = p.m * (p.n / 4);
+    hipLaunchKernelGGL(gemm_combine_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                       stream, p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace detattn

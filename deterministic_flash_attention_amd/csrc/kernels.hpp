@@ -75,6 +75,17 @@ struct MergeParams {
   float v_descale;
 };
 
+struct GemmParams {
+  const void* a;          // bf16 [m, lda]
+  const void* b;          // bf16 weight: [n, ldb] ([N, K] layout) or [k, ldb] ([K, N])
+  void* c;                // bf16 [m, ldc]
+  float* part;            // fp32 [nchunks, m, n]                 (split)
+  int64_t lda, ldb, ldc;  // row strides in elements
+  int64_t m, n, k;
+  int32_t nchunks;        // ceil(k / 1024)
+  int32_t tiles_m, tiles_n, group_m;  // set by the launcher (group_m: requested group)
+};
+
 // Each returns hipSuccess or the launch error.
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, bool fp8, bool split, bool paged,
                           hipStream_t stream);
@@ -83,5 +94,11 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool spl
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 
 int prefill_tile_rows(int head_dim, bool fp8);
+
+// GEMM: config selects the tile shape (0 .. gemm_num_configs() - 1); every
+// config computes the same bits.
+hipError_t launch_gemm(const GemmParams& p, int config, bool kn, bool split, hipStream_t stream);
+int gemm_num_configs();
+void gemm_config_tile(int config, int* bm, int* bn);
 
 }  // namespace detattn

@@ -11,6 +11,11 @@ Workload shapes (the five workloads of the method's pages, restated):
   * split-KV paged decode: 64 sequences x 1 token, Hq=32, Hkv=8, D=128,
                           context lengths uniform in [1, 32768], page size 16
   * fp8 wide-head prefill: B=1, Hq=Hkv=32, N=8192, D=192, e4m3 per-tensor scaled
+  * batch-invariant GEMM: the per-rank tensor-parallel (TP4) layer shapes of an
+    8B model that the method page times (M x K -> N): gate_up 4096 x 4096 ->
+    6144, down 4096 x 3072 -> 4096, and the decode-sized M = 8 qkv (4096 ->
+    1536) and gate_up (4096 -> 6144) products; bf16 N(0,1) activations and
+    weights
 
 All values are N(0,1) and unscaled (scaled fixtures hide corruption: ffpa-attn
 PR "fp8 attention D=192" page, section "Tests / docs").  Tensors are produced on
@@ -301,6 +306,38 @@ def extend_inputs(seed: int, ctx_lens: Sequence[int], q_lens: Sequence[int], hq:
                         table,
                         torch.tensor(ctx_lens, dtype=torch.int32), q_lens, ctx_lens, hq, hkv, d,
                         page_size, float(scale), bool(causal), dtype, qs, ks, vs, seed)
+
+
+# (name, M, N, K): C[M, N] = A[M, K] W^T with W [N, K]
+GEMM_SHAPES = [("gate_up", 4096, 6144, 4096), ("down", 4096, 4096, 3072),
+               ("qkv_decode", 8, 1536, 4096), ("gate_up_decode", 8, 6144, 4096)]
+
+
+@dataclasses.dataclass
+class GemmInputs:
+    a: torch.Tensor        # bf16 [M, lda] (rows of length K inside)
+    w: torch.Tensor        # bf16 [N, ldw] ([N, K] layout) or [K, ldw] ([K, N] layout)
+    m: int
+    n: int
+    k: int
+    weight_kn: bool
+    seed: int
+
+
+def gemm_inputs(seed: int, m: int, n: int, k: int, weight_kn: bool = False, pad_a: int = 0,
+                pad_w: int = 0, poison: bool = False) -> GemmInputs:
+    """N(0,1) bf16 operands.  pad_a / pad_w widen the row strides (lda = K + pad_a,
+    ldw = K or N + pad_w); with poison the padding holds NaN, which must never
+    reach a valid output."""
+    g = _gen(seed)
+    a = randn_bf16((m, k), g)
+    w = randn_bf16((k, n) if weight_kn else (n, k), g)
+    fill = float("nan") if poison else 0.0
+    if pad_a:
+        a = torch.cat([a, torch.full((m, pad_a), fill, dtype=torch.bfloat16)], dim=1)
+    if pad_w:
+        w = torch.cat([w, torch.full((w.shape[0], pad_w), fill, dtype=torch.bfloat16)], dim=1)
+    return GemmInputs(a, w, m, n, k, weight_kn, seed)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

@@ -9,6 +9,7 @@ import numpy as np
 import torch
 
 import oracle
+import oracle.gemm as ogemm
 import synth
 
 BF16_MAX_ABS, BF16_MEAN_ABS = 1e-2, 1e-3  # tolerances for bf16 inputs
@@ -150,3 +151,56 @@ def sample_rows(seqlens, per_seq: int, seed: int) -> np.ndarray:
             rows.extend(start + r for r in sorted(pick))
         start += n
     return np.array(rows, dtype=np.int64)
+
+
+# ---------------------------------------------------------------- GEMM
+def gemm_views(inp: synth.GemmInputs, device="cuda"):
+    """Device views of the (possibly row-padded) operands: A [M, K] with lda =
+    the stored width, W [N, K] or [K, N] likewise."""
+    a = inp.a.to(device)[:, :inp.k]
+    w = inp.w.to(device)
+    w = w[:, :inp.n] if inp.weight_kn else w[:, :inp.k]
+    return a, w
+
+
+def run_gemm(inp: synth.GemmInputs, schedule: int, config: int = -1, out=None, a=None):
+    import deterministic_flash_attention_amd as dfa
+    da, dw = gemm_views(inp)
+    if a is not None:
+        da = a
+    c = dfa.gemm(da, dw, dfa.WEIGHT_KN if inp.weight_kn else dfa.WEIGHT_NK, schedule=schedule,
+                 config=config, out=out)
+    torch.cuda.synchronize()
+    return c
+
+
+def oracle_gemm(inp: synth.GemmInputs, rows=None):
+    """fp64 product of the stored bf16 operands, and sum_k |a_ik| |b_kj| (the
+    scale of the accumulation error bound)."""
+    a = synth.to_f64(inp.a[:, :inp.k])
+    w = synth.to_f64(inp.w[:, :inp.n] if inp.weight_kn else inp.w[:, :inp.k])
+    if rows is not None:
+        a = a[rows]
+    return ogemm.gemm(a, w, not inp.weight_kn), ogemm.gemm(np.abs(a), np.abs(w), not inp.weight_kn)
+
+
+def compare_gemm(c_gpu: torch.Tensor, ref: np.ndarray, absprod: np.ndarray, k: int,
+                 rows=None, label: str = ""):
+    """Element-wise bound for one bf16 rounding of an fp32 sum of K exact bf16
+    products: |C - c| <= 2^-8 |c| + (1 + 2^-8) * 2 K 2^-24 * sum_k |a||b|
+    (2 K u32 covers any summation order of K terms, with room for
+    round-toward-zero additions inside the MFMA).  At least 97% of the elements
+    must equal the exact product rounded to bf16."""
+    g = c_gpu.float().cpu().double().numpy()
+    if rows is not None:
+        g = g[rows]
+    assert np.isfinite(g).all(), f"{label}: non-finite GPU output"
+    err = np.abs(g - ref)
+    bound = 2.0**-8 * np.abs(ref) + (1 + 2.0**-8) * 2 * k * 2.0**-24 * absprod
+    bad = err > bound
+    exact = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+    agree = float((g == exact).mean()) if g.size else 1.0
+    ratio = float((err / np.maximum(bound, 1e-300)).max()) if g.size else 0.0
+    note(f"{label}: max_err/bound={ratio:.3e} rounded-exact agreement={agree:.4f}")
+    assert not bad.any(), f"{label}: {int(bad.sum())} elements beyond the bound"
+    assert agree >= 0.97, f"{label}: only {agree:.4f} of elements equal the rounded exact value"

@@ -178,3 +178,79 @@ def test_zero_work_calls_return_ok_without_launch(lib):
     # batch 0 and zero rows are no-ops that succeed before any HIP call
     assert lib.attn_prefill_fwd(*_prefill_args(batch=0)) == DA_OK
     assert lib.attn_chunk_merge(None, 0, 0, 32, 0, 128, 1.0, None, None, None) == DA_OK
+
+
+# ---------------------------------------------------------------- GEMM boundary
+GEMM_HEADER = os.path.join(ROOT, "include", "detgemm.h")
+
+
+def gemm_declared_functions():
+    text = open(GEMM_HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\*?\s+\*?(det_gemm_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def test_gemm_header_declares_entry_points_and_library_exports_them(lib):
+    import deterministic_flash_attention_amd as dfa
+    names = gemm_declared_functions()
+    assert names == sorted(["det_gemm_num_chunks", "det_gemm_workspace_bytes",
+                            "det_gemm_num_configs", "det_gemm_config_tile", "det_gemm_fwd"])
+    out = subprocess.run(["nm", "-D", "--defined-only", dfa.library_path()], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\sT\s(det_gemm_\w+)", out))
+    for name in names:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_gemm_small_helpers(lib):
+    import deterministic_flash_attention_amd as dfa
+    assert [dfa.det_gemm_num_chunks(k) for k in (0, 1, 1024, 1025, 4096)] == [0, 1, 1, 2, 4]
+    assert dfa.det_gemm_workspace_bytes(8, 1536, 4096) == 4 * 8 * 1536 * 4
+    assert dfa.det_gemm_workspace_bytes(8, 1536, 0) == 0
+    assert dfa.det_gemm_workspace_bytes(-1, 8, 8) == 0
+    n = dfa.det_gemm_num_configs()
+    assert n >= 1
+    tiles = [dfa.det_gemm_config_tile(c) for c in range(n)]
+    assert all(bm % 32 == 0 and bn % 32 == 0 for bm, bn in tiles)
+    bm, bn = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert lib.det_gemm_config_tile(n, ctypes.byref(bm), ctypes.byref(bn)) == DA_EINVAL
+    assert lib.det_gemm_config_tile(-1, ctypes.byref(bm), ctypes.byref(bn)) == DA_EINVAL
+
+
+def _gemm_args(**over):
+    args = dict(a=FAKE, lda=4096, w=FAKE, ldw=4096, layout=0, c=FAKE, ldc=6144, m=4096, n=6144,
+                k=4096, schedule=0, config=-1, ws=None, ws_bytes=0, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(layout=2), DA_EINVAL),
+    (dict(schedule=2), DA_EINVAL),
+    (dict(m=-1), DA_EINVAL),
+    (dict(k=-8), DA_EINVAL),
+    (dict(config=99), DA_EINVAL),
+    (dict(config=-2), DA_EINVAL),
+    (dict(n=6140, ldc=6144), DA_EUNSUPPORTED),      # N not a multiple of 8
+    (dict(k=4092, lda=4096, ldw=4096), DA_EUNSUPPORTED),  # K not a multiple of 8
+    (dict(a=None), DA_EINVAL),
+    (dict(w=None), DA_EINVAL),
+    (dict(c=None), DA_EINVAL),
+    (dict(a=FAKE + 8), DA_EINVAL),                  # misaligned
+    (dict(lda=4000), DA_EINVAL),                    # lda < K
+    (dict(lda=4100), DA_EINVAL),                    # lda not a multiple of 8
+    (dict(ldw=4000), DA_EINVAL),                    # [N, K] weight: ldw < K
+    (dict(layout=1, ldw=4096), DA_EINVAL),          # [K, N] weight: ldw < N
+    (dict(ldc=6000), DA_EINVAL),                    # ldc < N
+    (dict(schedule=1), DA_EINVAL),                  # split without workspace
+    (dict(schedule=1, ws=FAKE, ws_bytes=100), DA_EWORKSPACE),
+    (dict(lda=1 << 24), DA_EUNSUPPORTED),           # a tile's byte extent beyond 2^31
+])
+def test_gemm_validation(lib, over, status):
+    assert lib.det_gemm_fwd(*_gemm_args(**over)) == status
+
+
+def test_gemm_zero_work_returns_ok_without_launch(lib):
+    assert lib.det_gemm_fwd(*_gemm_args(m=0, a=None, c=None)) == DA_OK
+    assert lib.det_gemm_fwd(*_gemm_args(n=0, w=None, c=None)) == DA_OK
