@@ -11,8 +11,11 @@ roofline of that kernel (HIP events on the stream it is launched on, against
 the 2.5 PFLOP/s dense bf16 MFMA peak) and the fp64 CPU oracle timed on a
 bounded sample of the same workload.  The other workloads (causal GQA varlen
 prefill, split-KV paged decode with its merge, fp8 D=192 prefill) are timed
-after it and reported under "secondary", decode against the 8 TB/s HBM peak.
-Inputs are seeded, synthetic and resident in HBM before timing starts.
+after it and reported under "secondary", decode against the 8 TB/s HBM peak,
+followed by the batch-invariant GEMM on four tensor-parallel layer shapes
+(torch.matmul, i.e. hipBLASLt, timed beside it as context; it does not follow
+the batch-invariant contract).  Inputs are seeded, synthetic and resident in
+HBM before timing starts.
 """
 from __future__ import annotations
 
@@ -238,6 +241,49 @@ def extend_entry(iters, warmup):
     }
 
 
+def gemm_entry(name, m, n, k, iters, warmup):
+    """C = A W^T for one layer shape: monolithic schedule for large M, split over
+    the 1024-wide chunks plus the combine pass for decode-sized M.  Large M is
+    priced against the bf16 MFMA peak (2 M N K FLOP), decode-sized M against
+    HBM (the weight, A and C bytes)."""
+    import torch
+    import deterministic_flash_attention_amd as dfa
+    import synth
+    inp = synth.gemm_inputs(0, m, n, k)
+    a, w = inp.a.cuda(), inp.w.cuda()
+    c = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    split = m <= 64
+    sched = dfa.SPLIT if split else dfa.MONOLITHIC
+    ws = torch.empty(max(dfa.det_gemm_workspace_bytes(m, n, k) // 4, 4), dtype=torch.float32,
+                     device="cuda")
+
+    def fn():
+        dfa.det_gemm_fwd(a, w, c, dfa.WEIGHT_NK, sched, -1, ws)
+    ms, _ = timed(fn, iters, warmup)
+    wt = w.t()
+    ms_ref, _ = timed(lambda: torch.matmul(a, wt), iters, warmup)
+    avg = sum(ms) / len(ms)
+    flops = 2 * m * n * k
+    tf = flops / (avg * 1e-3) / 1e12
+    nbytes = 2 * (m * k + n * k + m * n)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    if split:
+        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "traffic": counted_traffic(f"gemm_{name}"),
+                "kernel": "gemm split + combine (one step)"}
+    else:
+        roof = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / PEAK_BF16_TFLOPS, "traffic": counted_traffic(f"gemm_{name}"),
+                "kernel": "gemm monolithic"}
+    return {
+        "workload": f"gemm_{name}", "m": m, "n": n, "k": k, "dtype": "bf16",
+        "schedule": "split" if split else "monolithic", "flop": flops, "bytes": nbytes,
+        "ms_mean": avg, "ms_min": min(ms), "value": tf, "unit": "TFLOP/s", "gb_s": gbs,
+        "roofline": roof,
+        "context_torch_matmul_ms_min": min(ms_ref),
+    }
+
+
 def cpu_baseline(target_s: float = 12.0):
     """The fp64 oracle on a bounded row sample of the dense workload: as many
     query rows as fit about target_s seconds, all 32 heads, every key."""
@@ -287,6 +333,9 @@ def pmc_pass():
     fn, _ = run_prefill_fn(inp, t, dfa.MONOLITHIC)
     fn()
     decode_entry(1, 0)
+    for name, m, n, k in synth.GEMM_SHAPES:
+        inp_g = synth.gemm_inputs(0, m, n, k)
+        dfa.gemm(inp_g.a.cuda(), inp_g.w.cuda())
     torch.cuda.synchronize()
     print("pmc pass done")
 
@@ -337,6 +386,8 @@ def main():
                               "QK^T on fp8 MFMA, PV on bf16 MFMA: half the FLOPs at each peak")
             e["frac_of_bf16_peak"] = e["value"] / PEAK_BF16_TFLOPS
             secondary.append(e)
+        for name, m, n, k in synth.GEMM_SHAPES:
+            secondary.append(gemm_entry(name, m, n, k, 20, 3))
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     props = torch.cuda.get_device_properties(0)
     line = {

@@ -41,16 +41,24 @@ size_t partials_bytes_or_max(int64_t rows, int64_t hq, int64_t chunks, int64_t d
 
 int32_t gemm_chunks(int64_t k) { return k <= 0 ? 0 : (int32_t)((k + DG_CHUNK_K - 1) / DG_CHUNK_K); }
 
-// Tile shape when the caller leaves it open: the largest tile whose launch
-// (tiles x split factor) still covers the 256 compute units, else the one with
-// the most workgroups.  Every choice computes the same bits.
+// Tile shape when the caller leaves it open.  Every choice computes the same
+// bits.  The two large tiles want two workgroups per CU (512 launches or more):
+// 128 x 192 when N has no ragged 192-column tail, else 128 x 128.  Otherwise
+// the largest tile whose launch (tiles x split factor) still covers the 256
+// compute units, else the one with the most workgroups.
+int64_t gemm_launch_count(int32_t cfg, int64_t m, int64_t n, int64_t split_factor) {
+  int bm = 0, bn = 0;
+  detattn::gemm_config_tile(cfg, &bm, &bn);
+  return ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * split_factor;
+}
+
 int32_t gemm_auto_config(int64_t m, int64_t n, int64_t split_factor) {
-  int32_t best = 0;
+  if (n % 192 == 0 && gemm_launch_count(0, m, n, split_factor) >= 512) return 0;
+  if (gemm_launch_count(1, m, n, split_factor) >= 512) return 1;
+  int32_t best = 1;
   int64_t best_count = -1;
-  for (int32_t cfg = 0; cfg < detattn::gemm_num_configs(); ++cfg) {
-    int bm = 0, bn = 0;
-    detattn::gemm_config_tile(cfg, &bm, &bn);
-    const int64_t count = ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * split_factor;
+  for (int32_t cfg = 1; cfg < detattn::gemm_num_configs(); ++cfg) {
+    const int64_t count = gemm_launch_count(cfg, m, n, split_factor);
     if (count >= 256) return cfg;
     if (count > best_count) {
       best = cfg;

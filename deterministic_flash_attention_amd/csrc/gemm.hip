@@ -43,7 +43,7 @@ struct GemmCfg {
   static constexpr int kTM = BM / WM, kTN = BN / WN;  // wave tile
   static constexpr int kSM = kTM / 32, kSN = kTN / 32;
   static_assert(kTM % 32 == 0 && kTN % 32 == 0, "wave tiles are whole 32x32 MFMA tiles");
-  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 blocks in flight");
+  static_assert(STAGES >= 2 && STAGES <= 8, "2 to 8 blocks in flight");
   // A stage: BM rows of 128 bytes; loads per wave rounded up so every wave
   // issues the same count (the surplus lanes write zeros into the stage's tail).
   static constexpr int kAPer = cdiv(BM * 128, 1024 * kNW);
@@ -54,14 +54,14 @@ struct GemmCfg {
   static constexpr int kBPer = cdiv(kBRows * kBRow, 1024 * kNW);
   static constexpr int kBStage = kBPer * kNW * 1024;
   static constexpr int kStage = kAStage + kBStage;
-  // as many of the requested stages as fit in the 160 KB of LDS
-  static constexpr int kStages = STAGES * kStage <= 160 * 1024 ? STAGES : 160 * 1024 / kStage;
+  static constexpr int kPer = kAPer + kBPer;  // direct loads per wave per block
+  // As many of the requested stages as fit in the 160 KB of LDS and in the
+  // 6-bit vmcnt (the loads of kStages - 2 blocks stay in flight at a wait).
+  static constexpr int kStagesLds = STAGES * kStage <= 160 * 1024 ? STAGES : 160 * 1024 / kStage;
+  static constexpr int kStagesVm = 63 / kPer + 2;
+  static constexpr int kStages = kStagesLds < kStagesVm ? kStagesLds : kStagesVm;
   static_assert(kStages >= 2, "two stages must fit");
   static constexpr int kLds = kStages * kStage;
-  static constexpr int kPer = kAPer + kBPer;  // direct loads per wave per block
-  // Eight waves as two groups of four (4 x 2 wave grid) with three stages run
-  // the ping-pong schedule; the rest run all waves in lockstep.
-  static constexpr bool kPingPong = kNW == 8 && WM == 4 && kStages == 3;
 };
 
 // s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding).
@@ -69,6 +69,17 @@ template <int N>
 __device__ __forceinline__ void wait_vm_le() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// s_waitcnt vmcnt(ahead * PER) for a runtime ahead in [0, MAX].
+template <int MAX, int PER>
+__device__ __forceinline__ void wait_blocks_ahead(int ahead) {
+  if constexpr (MAX <= 0) {
+    wait_vm_le<0>();
+  } else {
+    if (ahead >= MAX) wait_vm_le<MAX * PER>();
+    else wait_blocks_ahead<MAX - 1, PER>(ahead);
+  }
 }
 
 // Workgroup barrier without the implicit memory fence of __syncthreads(): the
@@ -246,86 +257,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmParams p) 
   const int blk_end = min(c_end * kGemmBlocksPerChunk, nblocks_k);
   const int n = blk_end - blk_begin;
 
-  if constexpr (C::kPingPong) {
-    // Two groups of four waves, one per half of the tile's columns; wave w and
-    // wave w + 4 share a SIMD.  Group 1 runs one interval behind group 0, and
-    // every interval ends at a workgroup barrier, so on each SIMD one wave runs
-    // the 16 MFMAs of a block from registers while the other reads the next
-    // block's operands from LDS into registers and issues its share of the
-    // direct loads for the block two ahead.
-    //   interval 2j:   group 0 reads block j,  group 1 multiplies block j - 1
-    //   interval 2j+1: group 0 multiplies j,   group 1 reads block j
-    // Stage j is read in intervals 2j and 2j + 1 and refilled (block j + 3)
-    // from interval 2j + 2 on; before the barrier that opens interval 2j every
-    // wave has waited for its own loads of block j.
-    const int grp_id = wave >> 2;
-    u32x4 fa[4][C::kSM], fb[4][C::kSN];
-    if (n > 0) issue(blk_begin, 0);
-    if (n > 1) issue(blk_begin + 1, 1);
-    if (n > 1) wait_vm_le<C::kPer>();
-    else wait_vm_le<0>();
+  // Block j is published once every wave has its loads of it: at most the loads
+  // of the blocks issued after it (ahead of them) may still be in flight.
+#pragma unroll
+  for (int s = 0; s < C::kStages - 1; ++s)
+    if (s < n) issue(blk_begin + s, s);
+  for (int j = 0; j < n; ++j) {
+    wait_blocks_ahead<C::kStages - 2, C::kPer>(min(C::kStages - 2, n - 1 - j));
     barrier();
-    for (int t = 0; t <= 2 * n; ++t) {
-      const int my = t - grp_id;
-      if (my >= 0 && my < 2 * n) {
-        const int j = my >> 1;
-        if ((my & 1) == 0) {
-          const int st = j % 3;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-#pragma unroll
-            for (int i = 0; i < C::kSM; ++i) fa[s][i] = read_a(st, s, i);
-#pragma unroll
-            for (int jj = 0; jj < C::kSN; ++jj) fb[s][jj] = read_b(st, s, jj);
-          }
-          if (j + 2 < n) issue(blk_begin + j + 2, (j + 2) % 3);
-        } else {
-          __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-          for (int s = 0; s < 4; ++s)
-#pragma unroll
-            for (int i = 0; i < C::kSM; ++i)
-#pragma unroll
-              for (int jj = 0; jj < C::kSN; ++jj)
-                acc[i][jj] = mfma_bf16(fa[s][i], fb[s][jj], acc[i][jj]);
-          __builtin_amdgcn_s_setprio(0);
-          fold(blk_begin + j, j == n - 1);
-        }
-      }
-      if (t & 1) {
-        // publish block (t + 1) / 2 for the interval that opens next
-        const int jn = (t + 1) >> 1;
-        if (jn < n) {
-          if (jn + 1 < n) wait_vm_le<C::kPer>();
-          else wait_vm_le<0>();
-        }
-      }
-      barrier();
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < C::kStages - 1; ++s)
-      if (s < n) issue(blk_begin + s, s);
-    for (int j = 0; j < n; ++j) {
-      // Block j is published once every wave has its loads: at most the loads
-      // of the blocks issued after it may still be in flight.
-      const int ahead = min(C::kStages - 2, n - 1 - j);
-      if constexpr (C::kStages >= 4) {
-        if (ahead >= 2) wait_vm_le<2 * C::kPer>();
-        else if (ahead == 1) wait_vm_le<C::kPer>();
-        else wait_vm_le<0>();
-      } else if constexpr (C::kStages == 3) {
-        if (ahead >= 1) wait_vm_le<C::kPer>();
-        else wait_vm_le<0>();
-      } else {
-        wait_vm_le<0>();
-      }
-      barrier();
-      if (j + C::kStages - 1 < n)
-        issue(blk_begin + j + C::kStages - 1, (j + C::kStages - 1) % C::kStages);
-      compute(j % C::kStages);
-      fold(blk_begin + j, j == n - 1);
-    }
+    if (j + C::kStages - 1 < n)
+      issue(blk_begin + j + C::kStages - 1, (j + C::kStages - 1) % C::kStages);
+    compute(j % C::kStages);
+    fold(blk_begin + j, j == n - 1);
   }
 
   // ---- epilogue ---------------------------------------------------------------
@@ -410,10 +353,15 @@ hipError_t launch_cfg(const GemmParams& p0, bool kn, bool split, hipStream_t str
 
 }  // namespace
 
+// Tile configurations.  The two large ones run two workgroups of four waves on
+// each CU (80 KB and 64 KB of LDS), so one workgroup's barrier and load waits
+// overlap the other's MFMAs; the small ones serve few rows (decode), where a
+// workgroup streams one chunk of the weight and more blocks in flight hide the
+// memory latency.
 int gemm_num_configs() { return 5; }
 
 void gemm_config_tile(int config, int* bm, int* bn) {
-  static const int kTiles[5][2] = {{256, 128}, {128, 128}, {64, 64}, {32, 64}, {32, 32}};
+  static const int kTiles[5][2] = {{128, 192}, {128, 128}, {64, 64}, {32, 64}, {32, 32}};
   *bm = kTiles[config][0];
   *bn = kTiles[config][1];
 }
@@ -422,11 +370,11 @@ hipError_t launch_gemm(const GemmParams& p, int config, bool kn, bool split, hip
   if (p.m > 0 && p.n > 0 && p.nchunks > 0) {
     hipError_t e = hipSuccess;
     switch (config) {
-      case 0: e = launch_cfg<256, 128, 4, 2, 3>(p, kn, split, stream); break;
-      case 1: e = launch_cfg<128, 128, 2, 2, 3>(p, kn, split, stream); break;
-      case 2: e = launch_cfg<64, 64, 2, 2, 4>(p, kn, split, stream); break;
-      case 3: e = launch_cfg<32, 64, 1, 2, 4>(p, kn, split, stream); break;
-      case 4: e = launch_cfg<32, 32, 1, 1, 4>(p, kn, split, stream); break;
+      case 0: e = launch_cfg<128, 192, 2, 2, 2>(p, kn, split, stream); break;
+      case 1: e = launch_cfg<128, 128, 2, 2, 2>(p, kn, split, stream); break;
+      case 2: e = launch_cfg<64, 64, 2, 2, 6>(p, kn, split, stream); break;
+      case 3: e = launch_cfg<32, 64, 1, 2, 8>(p, kn, split, stream); break;
+      case 4: e = launch_cfg<32, 32, 1, 1, 8>(p, kn, split, stream); break;
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || !split) return e;
