@@ -303,7 +303,7 @@ struct PagedDirectStager {
   }
 };
 
-template <int D, bool FP8, int NW, int WPE, bool SPLIT, bool PAGED>
+template <int D, bool FP8, int NW, int WPE, bool SPLIT, bool PAGED, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void prefill_kernel(const PrefillParams p) {
   using G = Geom<D, FP8>;
@@ -366,7 +366,8 @@ void prefill_kernel(const PrefillParams p) {
   // bottom-right diagonal i + koff (causal, and a sliding window's left and
   // right edges).  Both bounds are nondecreasing in i.
   const int koff = lk - lq;
-  const int wl = p.window_left, wr = p.window_right;
+  // Without WIN the window bounds fold away at compile time (no window set).
+  const int wl = WIN ? p.window_left : -1, wr = WIN ? p.window_right : -1;
   auto row_lo = [&](int i) { return wl >= 0 ? max(0, i + koff - wl) : 0; };
   auto row_hi = [&](int i) {
     int hi = lk;
@@ -705,23 +706,31 @@ void prefill_kernel(const PrefillParams p) {
   }
 }
 
+template <int D, bool FP8, int NW, int WPE, bool WIN>
+hipError_t launch_win(const PrefillParams& p, bool split, bool paged, dim3 grid, dim3 block,
+                      hipStream_t stream) {
+  if (paged) {
+    if (split) {
+      hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, true, true, WIN>), grid, block, 0, stream, p);
+    } else {
+      hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, false, true, WIN>), grid, block, 0, stream, p);
+    }
+  } else if (split) {
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, true, false, WIN>), grid, block, 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, false, false, WIN>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
 template <int D, bool FP8, int NW, int WPE>
 hipError_t launch_one(const PrefillParams& p, bool split, bool paged, hipStream_t stream) {
   const long long per = (long long)p.batch * p.hq * p.tiles * (split ? p.cmax : 1);
   if (per <= 0) return hipSuccess;
   dim3 grid((unsigned)per), block(NW * kWave);
-  if (paged) {
-    if (split) {
-      hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, true, true>), grid, block, 0, stream, p);
-    } else {
-      hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, false, true>), grid, block, 0, stream, p);
-    }
-  } else if (split) {
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, true, false>), grid, block, 0, stream, p);
-  } else {
-    hipLaunchKernelGGL((prefill_kernel<D, FP8, NW, WPE, false, false>), grid, block, 0, stream, p);
-  }
-  return hipGetLastError();
+  if (p.window_left >= 0 || p.window_right >= 0)
+    return launch_win<D, FP8, NW, WPE, true>(p, split, paged, grid, block, stream);
+  return launch_win<D, FP8, NW, WPE, false>(p, split, paged, grid, block, stream);
 }
 
 // Per (head_dim, dtype): waves per workgroup and the waves per SIMD the
