@@ -20,8 +20,9 @@
 // global -> LDS with direct (buffer_load ... lds) loads, STAGES blocks in flight.
 // A and [N, K] B tiles keep 128-byte rows whose 16-byte chunks are XOR-swizzled
 // by (row / 2) % 8, so 16 consecutive rows read at one K offset hit 16 distinct
-// bank groups; a [K, N] B tile keeps 64 K rows padded by 64 bytes and is read
-// with the transposing LDS read.  Out-of-range rows, columns past a [K, N] row
+// bank groups; a [K, N] B tile keeps 64 K rows of BN columns, its 16-byte
+// granules XOR-swizzled by kn_swizzle(row) so the 4 rows x 64 bytes that half a
+// wave's transposing LDS read touches land in 16 distinct bank groups.  Out-of-range rows, columns past a [K, N] row
 // end and K past the end read as zero through the buffer range check.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -36,6 +37,17 @@ constexpr uint32_t kParkedOff = 0x80000000u;  // past every descriptor (offsets 
 
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Granule swizzle of a [K, N] B stage row r holding G = BN / 8 granules of 16
+// bytes: row r's base lies (r * G) % 16 granules into a 256-byte bank window,
+// and the XOR (which stays inside the row for these G) spreads the four rows a
+// half-wave reads over the 16 granules of the window.
+template <int G>
+__device__ __forceinline__ int kn_swizzle(int r) {
+  if constexpr (G % 16 == 0) return 4 * (r & 3);
+  else if constexpr (G % 16 == 8) return 4 * ((r >> 1) & 1);
+  else return 0;
+}
+
 template <int BM, int BN, int WM, int WN, int STAGES, bool KN>
 struct GemmCfg {
   static constexpr int kNW = WM * WN;
@@ -48,7 +60,8 @@ struct GemmCfg {
   // issues the same count (the surplus lanes write zeros into the stage's tail).
   static constexpr int kAPer = cdiv(BM * 128, 1024 * kNW);
   static constexpr int kAStage = kAPer * kNW * 1024;
-  static constexpr int kBRow = KN ? BN * 2 + 64 : 128;
+  static constexpr int kBRow = KN ? BN * 2 : 128;
+  static_assert(!KN || BN % 32 == 0, "a [K, N] row is whole 64-byte column groups");
   static constexpr int kBSlots = kBRow / 16;
   static constexpr int kBRows = KN ? kGemmBlockK : BN;
   static constexpr int kBPer = cdiv(kBRows * kBRow, 1024 * kNW);
@@ -92,7 +105,8 @@ __device__ __forceinline__ void barrier() {
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, bool KN, bool SPLIT>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmParams p) {
+// Two waves per SIMD: the large tiles run two workgroups per CU.
+__global__ __launch_bounds__(WM * WN * 64, 2) void gemm_kernel(const GemmParams p) {
   using C = GemmCfg<BM, BN, WM, WN, STAGES, KN>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::kLds];
 
@@ -146,8 +160,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmParams p) 
   for (int u = 0; u < C::kBPer; ++u) {
     const int pos = 64 * (wave + C::kNW * u) + lane;
     if constexpr (KN) {
-      const int r = pos / C::kBSlots, c = pos % C::kBSlots;
-      const bool ok = r < kGemmBlockK && c < BN / 8;
+      const int r = pos / C::kBSlots, c = (pos % C::kBSlots) ^ kn_swizzle<C::kBSlots>(r);
+      const bool ok = r < kGemmBlockK;
       boff[u] = ok ? (uint32_t)(r * p.ldb * 2 + 16 * c) : kParkedOff;
       bkidx[u] = ok ? r : (1 << 30);
     } else {
@@ -186,9 +200,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmParams p) 
   const uint32_t b_row = (uint32_t)((wn * C::kTN + l32) * 128);
   // [K, N] B through the transposing read: lane (group grp, li) addresses row
   // 16 s + 8 h + li / 4 (and 4 rows on), column base + 16 (grp % 2) + 4 (li % 4).
+  // Those rows agree in their two low bits (li / 4), so one swizzle serves every
+  // step; b_col[j] is the swizzled byte column of output tile j.
   const int grp = lane >> 4, li = lane & 15;
-  const uint32_t b_tr = (uint32_t)((8 * h + (li >> 2)) * C::kBRow +
-                                   (wn * C::kTN + 16 * (grp & 1) + 4 * (li & 3)) * 2);
+  const uint32_t b_tr = (uint32_t)((8 * h + (li >> 2)) * C::kBRow);
+  uint32_t b_col[C::kSN];
+#pragma unroll
+  for (int j = 0; j < C::kSN; ++j) {
+    const int cb = (wn * C::kTN + 32 * j + 16 * (grp & 1) + 4 * (li & 3)) * 2;
+    b_col[j] = (uint32_t)(16 * ((cb >> 4) ^ kn_swizzle<C::kBSlots>(li >> 2)) + (cb & 15));
+  }
 
   f32x16 acc[C::kSM][C::kSN];
   f32x16 tot[C::kSM][C::kSN];
@@ -207,7 +228,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(const GemmParams p) 
   auto read_b = [&](int st, int s, int j) -> u32x4 {
     const unsigned char* sb = smem + st * C::kStage + C::kAStage;
     if constexpr (KN) {
-      const uint32_t off = b_tr + (uint32_t)(16 * s * C::kBRow + 64 * j);
+      const uint32_t off = b_tr + (uint32_t)(16 * s * C::kBRow) + b_col[j];
       const u32x2 lo = __builtin_bit_cast(u32x2, lds_load_tr16(sb, off));
       const u32x2 hi = __builtin_bit_cast(u32x2, lds_load_tr16(sb, off + 4 * C::kBRow));
       return u32x4{lo[0], lo[1], hi[0], hi[1]};
