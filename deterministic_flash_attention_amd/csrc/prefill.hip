@@ -40,7 +40,13 @@ struct PrefillCfg {
   // widened on the way).
   static constexpr bool kDirect = !FP8 && (!PAGED || D <= 128);
   static constexpr int kThreads = NW * kWave;
-  static constexpr int kTileRows = 32 * NW;
+  // Wide heads on eight waves split D: waves w and w + kQGroups own the same 32
+  // query rows (both compute its scores and softmax) and each keeps half of
+  // the output columns, so a wave's accumulator and running total fit the 256
+  // registers of two waves per SIMD.
+  static constexpr int kDSplit = (D > 128 && NW == 8) ? 2 : 1;
+  static constexpr int kQGroups = NW / kDSplit;
+  static constexpr int kTileRows = 32 * kQGroups;
   static constexpr int kQBytes = kTileRows * G::kQRow;
   static constexpr int kBlockChunks = kBlockKeys * G::kChunks16;  // 16-B chunks per K block
   static constexpr int kPerThread = (kBlockChunks + kThreads - 1) / kThreads;
@@ -309,7 +315,8 @@ void prefill_kernel(const PrefillParams p) {
   using G = Geom<D, FP8>;
   using C = PrefillCfg<D, FP8, NW, PAGED>;
   static_assert(C::kLds <= 160 * 1024, "LDS budget of one gfx950 workgroup exceeded");
-  constexpr int NT = G::kDTiles;
+  constexpr int NT = G::kDTiles / C::kDSplit;  // output tiles of this wave
+  static_assert(G::kDTiles % C::kDSplit == 0, "D splits into whole 32-column tiles");
   __shared__ __attribute__((aligned(16))) unsigned char smem[C::kLds];
   unsigned char* const sQ = smem;
   unsigned char* const sK = smem + C::kKOff;
@@ -389,7 +396,9 @@ void prefill_kernel(const PrefillParams p) {
     blk_end = min(chunk * kBlocksPerChunk + kBlocksPerChunk, nblk);
   }
 
-  const int qrow = r0 + 32 * wave + (lane & 31);  // local query row of this lane
+  // Query group (32 rows) and output columns [32 dt0, 32 (dt0 + NT)) of this wave.
+  const int qg = wave % C::kQGroups, dt0 = (wave / C::kQGroups) * NT;
+  const int qrow = r0 + 32 * qg + (lane & 31);  // local query row of this lane
   const int lo = row_lo(qrow), hi = row_hi(qrow);
   // Blocks [wblk_first, wblk_end) hold a key visible to some row of this wave;
   // the others are fully masked for all of its rows (a wave whose rows all lie
@@ -397,7 +406,7 @@ void prefill_kernel(const PrefillParams p) {
   // they were (alpha = 1, p = 0, and acc, which starts at +0, is never -0, so
   // adding zero products changes no bit), so the wave skips its arithmetic
   // while still taking part in the staging and the barriers.
-  const int wrow0 = r0 + 32 * (int)uniform(wave);
+  const int wrow0 = r0 + 32 * ((int)uniform(wave) % C::kQGroups);
   const int wrow_last = min(wrow0 + 31, lq - 1);
   const bool wactive = wrow0 < lq;
   const int wlo = wactive ? row_lo(wrow0) : 0;
@@ -529,7 +538,7 @@ void prefill_kernel(const PrefillParams p) {
     wait_vm();
     __syncthreads();
     if (lag) __syncthreads();
-    const unsigned char* const sQw = sQ + (32 * wave) * G::kQRow;
+    const unsigned char* const sQw = sQ + (32 * qg) * G::kQRow;
     auto fold_chunk = [&]() {
       float ca, cb;
       int mode;
@@ -550,7 +559,7 @@ void prefill_kernel(const PrefillParams p) {
       const bool live = wave_live(blk);  // this wave computes block j
       __builtin_amdgcn_s_setprio(2);  // MFMA phase ahead of the other half's VALU
       if (j > 0) {
-        if (wave_live(blk - 1)) pv_mfma<D, NT>(acc, 0, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
+        if (wave_live(blk - 1)) pv_mfma<D, NT>(acc, dt0, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
         if constexpr (!SPLIT) {
           if (blk % kBlocksPerChunk == 0) fold_chunk();
         }
@@ -568,7 +577,7 @@ void prefill_kernel(const PrefillParams p) {
       wait_vm();
       __syncthreads();
     }
-    if (wave_live(blk_end - 1)) pv_mfma<D, NT>(acc, 0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
+    if (wave_live(blk_end - 1)) pv_mfma<D, NT>(acc, dt0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
     if constexpr (!SPLIT) fold_chunk();
     if (!lag) __syncthreads();
       } else {
@@ -604,7 +613,7 @@ void prefill_kernel(const PrefillParams p) {
     }
     __syncthreads();
 
-    const unsigned char* const sQw = sQ + (32 * wave) * G::kQRow;  // this wave's Q rows
+    const unsigned char* const sQw = sQ + (32 * qg) * G::kQRow;  // this wave's Q rows
     for (int j = 0; j < n; ++j) {
       const int blk = blk_begin + j, cur = j & 1;
       const bool more = j + 1 < n;
@@ -625,7 +634,7 @@ void prefill_kernel(const PrefillParams p) {
         float alpha;
         u32x4 pb[4];
         softmax(blk, s, alpha, pb);
-        pv_accumulate<D, NT>(acc, 0, alpha, pb, sV + cur * C::kVStage, lane);
+        pv_accumulate<D, NT>(acc, dt0, alpha, pb, sV + cur * C::kVStage, lane);
       }
       if constexpr (!SPLIT) {
         if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) {
@@ -661,7 +670,7 @@ void prefill_kernel(const PrefillParams p) {
     const rsrc_t mlr = make_rsrc(p.part_ml + 2 * ml_head,
                                  extent_bytes(lq, (int64_t)p.hq * 8, 8,
                                               ((int64_t)(chunk + 1) * p.total_q * p.hq - ml_head) * 8));
-    buf_store8(mlr, h ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 8),
+    buf_store8(mlr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 8),
                u32x2{f32_bits(m), f32_bits(l)});
     const int64_t acc_head = ml_head * D;
     const rsrc_t ar = make_rsrc(p.part_acc + acc_head,
@@ -672,7 +681,7 @@ void prefill_kernel(const PrefillParams p) {
     for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * j + 8 * q4 + 4 * h;
+        const int d = 32 * (dt0 + j) + 8 * q4 + 4 * h;
         buf_store16(ar, rowoff + (uint32_t)d * 4u,
                     u32x4{f32_bits(acc[j][4 * q4 + 0]),
                           f32_bits(acc[j][4 * q4 + 1]),
@@ -690,7 +699,7 @@ void prefill_kernel(const PrefillParams p) {
     for (int j = 0; j < NT; ++j)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * j + 8 * q4 + 4 * h;
+        const int d = 32 * (dt0 + j) + 8 * q4 + 4 * h;
         const uint32_t w0 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 0], L, vd),
                                         finalize_elem(A[j][4 * q4 + 1], L, vd));
         const uint32_t w1 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 2], L, vd),
@@ -700,7 +709,7 @@ void prefill_kernel(const PrefillParams p) {
     if (p.lse != nullptr) {
       const rsrc_t lr = make_rsrc(p.lse + o_head, extent_bytes(lq, (int64_t)p.hq * 4, 4,
                                                                (p.total_q * p.hq - o_head) * 4));
-      buf_store4(lr, h ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 4),
+      buf_store4(lr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 4),
                  f32_bits(finalize_lse(M, L)));
     }
   }
@@ -736,12 +745,20 @@ hipError_t launch_one(const PrefillParams& p, bool split, bool paged, hipStream_
 // Per (head_dim, dtype): waves per workgroup and the waves per SIMD the
 // register budget targets.  Eight waves (two per SIMD, so one wave's MFMAs can
 // fill the other's gaps) up to D = 128, where a wave fits in the 256 registers
-// that leaves it; four waves (one per SIMD) for wider heads.
+// that leaves it, and for fp8 D = 192, whose waves split the output columns
+// (its scores are cheap on the 64-wide fp8 MFMA, so computing them twice costs
+// less than a SIMD without a second wave); four waves (one per SIMD) for bf16
+// D = 192.
 template <int D, bool FP8>
 struct Layout {
-  static constexpr int kWaves = D <= 128 ? 8 : 4;
-  static constexpr int kWavesPerEU = D <= 128 ? 2 : 1;
+  static constexpr int kWaves = (D <= 128 || FP8) ? 8 : 4;
+  static constexpr int kWavesPerEU = (D <= 128 || FP8) ? 2 : 1;
 };
+
+template <int D, bool FP8>
+constexpr int tile_rows() {
+  return PrefillCfg<D, FP8, Layout<D, FP8>::kWaves>::kTileRows;
+}
 
 template <int D, bool FP8>
 hipError_t launch_layout(const PrefillParams& p, bool split, bool paged, hipStream_t stream) {
@@ -753,9 +770,9 @@ hipError_t launch_layout(const PrefillParams& p, bool split, bool paged, hipStre
 
 int prefill_tile_rows(int head_dim, bool fp8) {
   switch (head_dim) {
-    case 64: return 32 * (fp8 ? Layout<64, true>::kWaves : Layout<64, false>::kWaves);
-    case 128: return 32 * (fp8 ? Layout<128, true>::kWaves : Layout<128, false>::kWaves);
-    case 192: return 32 * (fp8 ? Layout<192, true>::kWaves : Layout<192, false>::kWaves);
+    case 64: return fp8 ? tile_rows<64, true>() : tile_rows<64, false>();
+    case 128: return fp8 ? tile_rows<128, true>() : tile_rows<128, false>();
+    case 192: return fp8 ? tile_rows<192, true>() : tile_rows<192, false>();
     default: return 32 * 8;
   }
 }
