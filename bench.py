@@ -157,14 +157,15 @@ def decode_bytes(inp) -> int:
     return kv + b * hq * d * es + b * hq * d * 2 + 4 * int(pages.sum()) + 4 * b
 
 
-def decode_entry(iters, warmup):
+def decode_entry(iters, warmup, dtype="bf16"):
+    """The paged decode workload (bf16, or an e4m3 cache with per-tensor scales)."""
     import torch
     import deterministic_flash_attention_amd as dfa
     import synth
     cfg = synth.PAGED_DECODE
     inp = synth.decode_inputs(0, cfg["batch"], cfg["hq"], cfg["hkv"], cfg["d"],
                               ctx_min=cfg["ctx_min"], ctx_max=cfg["ctx_max"],
-                              spare_pages=cfg["spare_pages"], poison=False)
+                              spare_pages=cfg["spare_pages"], poison=False, dtype=dtype)
     dev = torch.device("cuda")
     q, kc, vc = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev)
     pt, cl = inp.page_table.to(dev), inp.context_lens.to(dev)
@@ -174,11 +175,14 @@ def decode_entry(iters, warmup):
     part = torch.empty(dfa.attn_partials_bytes(b, hq, cmax, d) // 4, dtype=torch.float32, device=dev)
     o = torch.empty(b, hq, d, dtype=torch.bfloat16, device=dev)
 
+    desc = (inp.q_scale, inp.k_scale, inp.v_scale)
+
     def split():
-        dfa.attn_decode_split_fwd(q, kc, vc, pt, cl, mc, inp.scale, dfa.SPLIT, partials=part)
+        dfa.attn_decode_split_fwd(q, kc, vc, pt, cl, mc, inp.scale, dfa.SPLIT, partials=part,
+                                  descales=desc)
 
     def merge():
-        dfa.attn_chunk_merge(part, b, hq, cmax, d, o)
+        dfa.attn_chunk_merge(part, b, hq, cmax, d, o, v_descale=desc[2])
 
     def both():
         split()
@@ -193,14 +197,15 @@ def decode_entry(iters, warmup):
     gbs_split = nbytes / (a_split * 1e-3) / 1e9
     part_bytes = int((inp.context_lens.long() + 511).div(512, rounding_mode="floor").sum()) * hq * (d + 2) * 4
     return {
-        "workload": "paged_decode", "batch": b, "hq": hq, "hkv": inp.hkv, "d": d,
+        "workload": "paged_decode" if dtype == "bf16" else "paged_decode_fp8", "dtype": dtype,
+        "batch": b, "hq": hq, "hkv": inp.hkv, "d": d,
         "sum_context": int(inp.context_lens.sum()), "bytes": nbytes,
         "ms_split": a_split, "ms_merge": sum(ms_merge) / iters, "ms_step": a_step,
         "value": gbs_step, "unit": "GB/s",
         "partials_bytes_written": part_bytes,
         "roofline": {"bound": "hbm", "achieved": gbs_split, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs_split / PEAK_HBM_GBS,
-                     "traffic": counted_traffic("decode_split_bf16"),
+                     "traffic": counted_traffic("decode_split_bf16") if dtype == "bf16" else None,
                      "kernel": "decode split"},
         "step_frac_of_hbm": gbs_step / PEAK_HBM_GBS,
     }
@@ -376,6 +381,7 @@ def main():
         secondary.append(prefill_entry("causal_gqa_varlen", synth.CAUSAL_VARLEN, True, "bf16",
                                        20, 3, PEAK_BF16_TFLOPS, "bf16 dense MFMA"))
         secondary.append(decode_entry(20, 3))
+        secondary.append(decode_entry(20, 3, dtype="fp8"))
         secondary.append(extend_entry(20, 3))
         secondary.append(prefill_entry("sliding_window_1024", synth.DENSE_PREFILL, True, "bf16",
                                        20, 3, PEAK_BF16_TFLOPS, "bf16 dense MFMA",
