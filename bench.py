@@ -158,7 +158,9 @@ def decode_bytes(inp) -> int:
 
 
 def decode_entry(iters, warmup, dtype="bf16"):
-    """The paged decode workload (bf16, or an e4m3 cache with per-tensor scales)."""
+    """The paged decode workload (bf16, or an e4m3 cache with per-tensor scales),
+    cache pages stored heads-outer ("HND": each kv head's 16 page rows contiguous,
+    5% faster than tokens-outer "NHD", timed beside it; the same bits)."""
     import torch
     import deterministic_flash_attention_amd as dfa
     import synth
@@ -167,7 +169,9 @@ def decode_entry(iters, warmup, dtype="bf16"):
                               ctx_min=cfg["ctx_min"], ctx_max=cfg["ctx_max"],
                               spare_pages=cfg["spare_pages"], poison=False, dtype=dtype)
     dev = torch.device("cuda")
-    q, kc, vc = inp.q.to(dev), inp.k_cache.to(dev), inp.v_cache.to(dev)
+    q = inp.q.to(dev)
+    kc = inp.k_cache.permute(0, 2, 1, 3).contiguous().to(dev)
+    vc = inp.v_cache.permute(0, 2, 1, 3).contiguous().to(dev)
     pt, cl = inp.page_table.to(dev), inp.context_lens.to(dev)
     b, hq, d = inp.q.shape
     mc = int(inp.context_lens.max())
@@ -179,7 +183,7 @@ def decode_entry(iters, warmup, dtype="bf16"):
 
     def split():
         dfa.attn_decode_split_fwd(q, kc, vc, pt, cl, mc, inp.scale, dfa.SPLIT, partials=part,
-                                  descales=desc)
+                                  descales=desc, kv_layout="HND")
 
     def merge():
         dfa.attn_chunk_merge(part, b, hq, cmax, d, o, v_descale=desc[2])
@@ -190,6 +194,14 @@ def decode_entry(iters, warmup, dtype="bf16"):
     ms_split, _ = timed(split, iters, warmup)
     ms_merge, _ = timed(merge, iters, warmup)
     ms_step, _ = timed(both, iters, warmup)
+    kc_nhd, vc_nhd = inp.k_cache.to(dev), inp.v_cache.to(dev)
+
+    def both_nhd():
+        dfa.attn_decode_split_fwd(q, kc_nhd, vc_nhd, pt, cl, mc, inp.scale, dfa.SPLIT,
+                                  partials=part, descales=desc, kv_layout="NHD")
+        merge()
+    ms_step_nhd, _ = timed(both_nhd, iters, warmup)
+    del kc_nhd, vc_nhd
     nbytes = decode_bytes(inp)
     a_split = sum(ms_split) / iters
     a_step = sum(ms_step) / iters
@@ -198,7 +210,8 @@ def decode_entry(iters, warmup, dtype="bf16"):
     part_bytes = int((inp.context_lens.long() + 511).div(512, rounding_mode="floor").sum()) * hq * (d + 2) * 4
     return {
         "workload": "paged_decode" if dtype == "bf16" else "paged_decode_fp8", "dtype": dtype,
-        "batch": b, "hq": hq, "hkv": inp.hkv, "d": d,
+        "batch": b, "hq": hq, "hkv": inp.hkv, "d": d, "kv_layout": "HND",
+        "step_frac_of_hbm_nhd": nbytes / (sum(ms_step_nhd) / iters * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "sum_context": int(inp.context_lens.sum()), "bytes": nbytes,
         "ms_split": a_split, "ms_merge": sum(ms_merge) / iters, "ms_step": a_step,
         "value": gbs_step, "unit": "GB/s",

@@ -157,17 +157,30 @@ def attn_prefill_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max
     _check("attn_prefill_fwd", st)
 
 
+def _cache_geometry(k_cache, kv_layout: str):
+    """(num_pages, page_size, Hkv, D) and the (page, token, head) element strides of a
+    contiguous paged cache: "NHD" is [num_pages, 16, Hkv, D] (tokens outer), "HND" is
+    [num_pages, Hkv, 16, D] (heads outer, each head's page rows contiguous)."""
+    if kv_layout == "NHD":
+        npages, psize, hkv, d = k_cache.shape
+        return npages, psize, hkv, d, psize * hkv * d, hkv * d, d
+    if kv_layout == "HND":
+        npages, hkv, psize, d = k_cache.shape
+        return npages, psize, hkv, d, hkv * psize * d, d, psize * d
+    raise ValueError(f"kv_layout must be 'NHD' or 'HND', not {kv_layout!r}")
+
+
 def attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
                           softmax_scale: float, schedule: int = SPLIT, partials=None, o=None,
                           lse=None, descales=(1.0, 1.0, 1.0), window_left: int = -1,
-                          stream=None) -> None:
-    """Mirror of the C ``attn_decode_split_fwd`` for caches shaped
-    [num_pages, 16, Hkv, D] (contiguous)."""
+                          stream=None, kv_layout: str = "NHD") -> None:
+    """Mirror of the C ``attn_decode_split_fwd`` for contiguous caches in the
+    "NHD" [num_pages, 16, Hkv, D] or "HND" [num_pages, Hkv, 16, D] layout."""
     lib = load_library()
-    npages, psize, hkv, d = k_cache.shape
+    npages, psize, hkv, d, s_page, s_tok, s_head = _cache_geometry(k_cache, kv_layout)
     st = lib.attn_decode_split_fwd(
         _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(npages),
-        int(psize * hkv * d), int(hkv * d), int(d), _ptr(page_table), int(page_table.shape[1]),
+        int(s_page), int(s_tok), int(s_head), _ptr(page_table), int(page_table.shape[1]),
         _ptr(context_lens), int(max_context_len), int(window_left), int(q.shape[0]), int(psize),
         int(q.shape[1]), int(hkv), int(d), float(softmax_scale), float(descales[0]),
         float(descales[1]),
@@ -181,14 +194,14 @@ def attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context
                           max_seqlen_q: int, max_context_len: int, softmax_scale: float,
                           causal: bool, schedule: int = MONOLITHIC, o=None, lse=None,
                           partials=None, descales=(1.0, 1.0, 1.0), window=(-1, -1),
-                          stream=None) -> None:
-    """Mirror of the C ``attn_paged_extend_fwd`` for caches shaped
-    [num_pages, 16, Hkv, D] (contiguous)."""
+                          stream=None, kv_layout: str = "NHD") -> None:
+    """Mirror of the C ``attn_paged_extend_fwd`` for contiguous caches in the
+    "NHD" [num_pages, 16, Hkv, D] or "HND" [num_pages, Hkv, 16, D] layout."""
     lib = load_library()
-    npages, psize, hkv, d = k_cache.shape
+    npages, psize, hkv, d, s_page, s_tok, s_head = _cache_geometry(k_cache, kv_layout)
     st = lib.attn_paged_extend_fwd(
         _dtype_code(q), _ptr(q), _ptr(cu_seqlens_q), _ptr(k_cache), _ptr(v_cache), int(npages),
-        int(psize * hkv * d), int(hkv * d), int(d), _ptr(page_table), int(page_table.shape[1]),
+        int(s_page), int(s_tok), int(s_head), _ptr(page_table), int(page_table.shape[1]),
         _ptr(context_lens), int(cu_seqlens_q.numel() - 1), int(max_seqlen_q),
         int(max_context_len), int(q.shape[0]), int(psize), int(q.shape[1]), int(hkv), int(d),
         float(softmax_scale), int(bool(causal)), int(window[0]), int(window[1]),
@@ -308,8 +321,9 @@ def decode(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
            softmax_scale: Optional[float] = None, schedule: int = SPLIT,
            descales=(1.0, 1.0, 1.0), out: Optional[torch.Tensor] = None,
            return_lse: bool = False, partials: Optional[torch.Tensor] = None,
-           window_left: int = -1, stream=None):
-    """Single-token paged decode; returns O (bf16) and optionally lse."""
+           window_left: int = -1, stream=None, kv_layout: str = "NHD"):
+    """Single-token paged decode; returns O (bf16) and optionally lse.  kv_layout
+    "NHD" ([num_pages, 16, Hkv, D]) or "HND" ([num_pages, Hkv, 16, D]): the same bits."""
     b, hq, d = q.shape
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
@@ -320,12 +334,12 @@ def decode(q, k_cache, v_cache, page_table, context_lens, max_context_len: int,
         part = partials if partials is not None else _new_partials(b, hq, cmax, d, q.device)
         attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len,
                               softmax_scale, SPLIT, partials=part, descales=descales,
-                              window_left=window_left, stream=stream)
+                              window_left=window_left, stream=stream, kv_layout=kv_layout)
         attn_chunk_merge(part, b, hq, cmax, d, o, lse, v_descale=descales[2], stream=stream)
     else:
         attn_decode_split_fwd(q, k_cache, v_cache, page_table, context_lens, max_context_len,
                               softmax_scale, MONOLITHIC, o=o, lse=lse, descales=descales,
-                              window_left=window_left, stream=stream)
+                              window_left=window_left, stream=stream, kv_layout=kv_layout)
     return (o, lse) if return_lse else o
 
 
@@ -333,7 +347,7 @@ def paged_extend(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens, ma
                  max_context_len: int, causal: bool, softmax_scale: Optional[float] = None,
                  schedule: int = MONOLITHIC, descales=(1.0, 1.0, 1.0),
                  out: Optional[torch.Tensor] = None, return_lse: bool = False, window=(-1, -1),
-                 stream=None):
+                 stream=None, kv_layout: str = "NHD"):
     """Mixed prefill / extend / decode batch over a paged KV cache; returns O
     (bf16) and optionally lse.  Sequence b's rows are its last
     cu_seqlens_q[b+1] - cu_seqlens_q[b] tokens of context_lens[b]."""
@@ -347,10 +361,12 @@ def paged_extend(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens, ma
         part = _new_partials(tq, hq, cmax, d, q.device)
         attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
                               max_seqlen_q, max_context_len, softmax_scale, causal, SPLIT,
-                              partials=part, descales=descales, window=window, stream=stream)
+                              partials=part, descales=descales, window=window, stream=stream,
+                              kv_layout=kv_layout)
         attn_chunk_merge(part, tq, hq, cmax, d, o, lse, v_descale=descales[2], stream=stream)
     else:
         attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
                               max_seqlen_q, max_context_len, softmax_scale, causal, MONOLITHIC,
-                              o=o, lse=lse, descales=descales, window=window, stream=stream)
+                              o=o, lse=lse, descales=descales, window=window, stream=stream,
+                              kv_layout=kv_layout)
     return (o, lse) if return_lse else o

@@ -254,3 +254,15 @@ def test_gemm_validation(lib, over, status):
 def test_gemm_zero_work_returns_ok_without_launch(lib):
     assert lib.det_gemm_fwd(*_gemm_args(m=0, a=None, c=None)) == DA_OK
     assert lib.det_gemm_fwd(*_gemm_args(n=0, w=None, c=None)) == DA_OK
+
+
+def test_cache_layout_strides():
+    """The Python mirror's element strides for the two paged-cache layouts."""
+    import torch
+    import deterministic_flash_attention_amd as dfa
+    nhd = torch.empty(10, 16, 8, 128)
+    hnd = torch.empty(10, 8, 16, 128)
+    assert dfa._cache_geometry(nhd, "NHD") == (10, 16, 8, 128, 16 * 8 * 128, 8 * 128, 128)
+    assert dfa._cache_geometry(hnd, "HND") == (10, 16, 8, 128, 8 * 16 * 128, 128, 16 * 128)
+    with pytest.raises(ValueError):
+        dfa._cache_geometry(nhd, "NDH")
