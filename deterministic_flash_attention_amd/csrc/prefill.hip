@@ -342,7 +342,31 @@ void prefill_kernel(const PrefillParams p) {
     head = id % p.hq;
     id /= p.hq;
   }
-  const int b = id % p.batch;
+  int b = id % p.batch;
+  if constexpr (PAGED && !SPLIT) {
+    // A mixed batch can hold a decode or short extend whose single tile scans a
+    // long context; handed out last, that tile alone would run past everything
+    // else.  Sequences are therefore dealt in descending context length (ties by
+    // index): the rank-th longest sequence takes this workgroup's batch slot.
+    // Which workgroup computes a tile changes no bit of its result.
+    __shared__ int sCtx[C::kThreads];
+    __shared__ int sSeq;
+    if (p.batch <= C::kThreads) {
+      if (tid < p.batch) sCtx[tid] = p.ctx_lens[tid];
+      __syncthreads();
+      if (tid < p.batch) {
+        const int key = sCtx[tid];
+        int rank = 0;
+        for (int t = 0; t < p.batch; ++t) {
+          const int kt = sCtx[t];
+          rank += (kt > key || (kt == key && t < tid)) ? 1 : 0;
+        }
+        if (rank == b) sSeq = tid;
+      }
+      __syncthreads();
+      b = sSeq;
+    }
+  }
   id /= p.batch;
   int chunk = 0;
   if constexpr (SPLIT) {
