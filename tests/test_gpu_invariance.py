@@ -50,7 +50,8 @@ def test_split_equals_monolithic_decode(dtype):
     assert_bitwise(l1, l2, "decode lse split vs monolithic")
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp8", 192)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("bf16", 192), ("fp8", 192),
+                                     ("fp8", 128), ("fp8", 64)])
 def test_decode_equals_last_prefill_row(dtype, d):
     """The decode token of a sequence of length L equals row L-1 of its causal
     prefill, bit for bit, for lengths around block and chunk boundaries."""
