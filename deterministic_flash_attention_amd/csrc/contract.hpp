@@ -77,6 +77,8 @@ __device__ __forceinline__ int key_sigma(int r) {
 __device__ __forceinline__ int score_key(int t, int i, int h) {
   return 32 * t + 16 * (i >> 3) + 8 * h + (i & 7);
 }
+// score_key without the half-wave's 8h: a compile-time constant in 0..63.
+constexpr int score_key_base(int t, int i) { return 32 * t + 16 * (i >> 3) + (i & 7); }
 
 // S^T = K_blk Q^T for the 64 keys of the staged block; s[t] holds key tile t.
 // qrow points at the lane's query row in LDS (D elements of Q).  K rows sit in
@@ -121,6 +123,29 @@ __device__ __forceinline__ void qk_scores_qrow(f32x16 (&s)[2], const unsigned ch
   }
 }
 
+// bf16 S^T with the lane's Q^T operands already in registers (q[st] is what
+// qk_scores_qrow reads from the Q row for K-step st): the same MFMA sequence.
+template <int D, int KPAGE = 16 * Geom<D, false>::kKRow>
+__device__ __forceinline__ void qk_scores_qreg(f32x16 (&s)[2], const u32x4 (&q)[D / 16],
+                                               const unsigned char* ks, int lane) {
+  using G = Geom<D, false>;
+  const int row = key_sigma(lane & 31);
+  const int h = lane >> 5;
+  const int krow = (row >> 4) * KPAGE + (row & 15) * G::kKRow;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < G::kSteps; ++st) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t off = (uint32_t)(krow + 2 * t * KPAGE + (16 * st + 8 * h) * G::kEs);
+      s[t] = mfma_bf16(lds_load16(ks, off), q[st], s[t]);
+    }
+  }
+}
+
 // Same product with the Q^T operands read from the wave's rows of the LDS Q tile
 // (qs points at the wave's first row; row stride G::kQRow).
 template <int D, bool FP8, int KPAGE = 16 * Geom<D, FP8>::kKRow>
@@ -155,16 +180,18 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
                                               u32x4 (&pb)[4]) {
   // Phases 0-1: mask by select and row max on the raw dot products.  fl(c*s)
   // is monotonic in s for c > 0, so fl(c * max s) is exactly the max of the
-  // scaled scores.
+  // scaled scores.  The key bounds are shifted by the half-wave's 8h once, so
+  // each test compares score_key - 8h, an inline constant, with them.
+  const int hi_h = rel_hi - 8 * h, lo_h = rel_lo - 8 * h;
   float x[2][16];
   float mr0 = -INFINITY, mr1 = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float v = s[0][i];
-    if (MASK == kMaskHi) v = (score_key(0, i, h) < rel_hi) ? v : -INFINITY;
+    if (MASK == kMaskHi) v = (score_key_base(0, i) < hi_h) ? v : -INFINITY;
     if (MASK == kMaskLoHi) {
-      const int key = score_key(0, i, h);
-      v = (key >= rel_lo && key < rel_hi) ? v : -INFINITY;
+      const int key = score_key_base(0, i);
+      v = (key >= lo_h && key < hi_h) ? v : -INFINITY;
     }
     x[0][i] = v;
     mr0 = fmaxf(mr0, v);
@@ -172,10 +199,10 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     float v = s[1][i];
-    if (MASK == kMaskHi) v = (score_key(1, i, h) < rel_hi) ? v : -INFINITY;
+    if (MASK == kMaskHi) v = (score_key_base(1, i) < hi_h) ? v : -INFINITY;
     if (MASK == kMaskLoHi) {
-      const int key = score_key(1, i, h);
-      v = (key >= rel_lo && key < rel_hi) ? v : -INFINITY;
+      const int key = score_key_base(1, i);
+      v = (key >= lo_h && key < hi_h) ? v : -INFINITY;
     }
     x[1][i] = v;
     mr1 = fmaxf(mr1, v);

@@ -563,6 +563,13 @@ void prefill_kernel(const PrefillParams p) {
     __syncthreads();
     if (lag) __syncthreads();
     const unsigned char* const sQw = sQ + (32 * qg) * G::kQRow;
+    // bf16: the wave's Q^T operands move from the LDS tile to registers once.
+    u32x4 qop[FP8 ? 1 : D / 16];
+    if constexpr (!FP8) {
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st)
+        qop[st] = lds_load16(sQw + (lane & 31) * G::kQRow, (uint32_t)((16 * st + 8 * h) * 2));
+    }
     auto fold_chunk = [&]() {
       float ca, cb;
       int mode;
@@ -589,7 +596,13 @@ void prefill_kernel(const PrefillParams p) {
         }
       }
       f32x16 s[2];
-      if (live) qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + (j & 1) * C::kKStage, lane);
+      if (live) {
+        if constexpr (FP8) {
+          qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + (j & 1) * C::kKStage, lane);
+        } else {
+          qk_scores_qreg<D, C::kKPage>(s, qop, sK + (j & 1) * C::kKStage, lane);
+        }
+      }
       __syncthreads();
       __builtin_amdgcn_s_setprio(0);
       event(j + lag);
