@@ -123,12 +123,29 @@ __device__ __forceinline__ void qk_scores_qrow(f32x16 (&s)[2], const unsigned ch
   }
 }
 
-// bf16 S^T with the lane's Q^T operands already in registers (q[st] is what
-// qk_scores_qrow reads from the Q row for K-step st): the same MFMA sequence.
-template <int D, int KPAGE = 16 * Geom<D, false>::kKRow>
-__device__ __forceinline__ void qk_scores_qreg(f32x16 (&s)[2], const u32x4 (&q)[D / 16],
+// The lane's Q^T operands for every K-step of qk_scores_qrow, read once from
+// its Q row: bf16 one u32x4 per 16-wide step, e4m3 two per 64-wide step.
+template <int D, bool FP8>
+struct QOperands {
+  static constexpr int kCount = FP8 ? 2 * (D / 64) : D / 16;
+  u32x4 q[kCount];
+  __device__ __forceinline__ void load(const unsigned char* qrow, int lane) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int st = 0; st < kCount; ++st) {
+      const uint32_t off = FP8 ? (uint32_t)(64 * (st >> 1) + 32 * h + 16 * (st & 1))
+                               : (uint32_t)((16 * st + 8 * h) * 2);
+      q[st] = lds_load16(qrow, off);
+    }
+  }
+};
+
+// qk_scores_qrow with the Q^T operands already in registers: the same MFMA
+// sequence on the same operand values.
+template <int D, bool FP8, int KPAGE = 16 * Geom<D, FP8>::kKRow>
+__device__ __forceinline__ void qk_scores_qreg(f32x16 (&s)[2], const QOperands<D, FP8>& qo,
                                                const unsigned char* ks, int lane) {
-  using G = Geom<D, false>;
+  using G = Geom<D, FP8>;
   const int row = key_sigma(lane & 31);
   const int h = lane >> 5;
   const int krow = (row >> 4) * KPAGE + (row & 15) * G::kKRow;
@@ -136,12 +153,24 @@ __device__ __forceinline__ void qk_scores_qreg(f32x16 (&s)[2], const u32x4 (&q)[
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[t][i] = 0.0f;
+  if constexpr (FP8) {
 #pragma unroll
-  for (int st = 0; st < G::kSteps; ++st) {
+    for (int st = 0; st < D / 64; ++st) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t off = (uint32_t)(krow + 2 * t * KPAGE + (16 * st + 8 * h) * G::kEs);
-      s[t] = mfma_bf16(lds_load16(ks, off), q[st], s[t]);
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t off = (uint32_t)(krow + 2 * t * KPAGE + 64 * st + 32 * h);
+        s[t] = mfma_fp8x64(lds_load16(ks, off), lds_load16(ks, off + 16), qo.q[2 * st],
+                           qo.q[2 * st + 1], s[t]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < G::kSteps; ++st) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t off = (uint32_t)(krow + 2 * t * KPAGE + (16 * st + 8 * h) * G::kEs);
+        s[t] = mfma_bf16(lds_load16(ks, off), qo.q[st], s[t]);
+      }
     }
   }
 }

@@ -39,6 +39,9 @@ struct PrefillCfg {
   // where the page-aligned stages fit); otherwise through registers (fp8 V is
   // widened on the way).
   static constexpr bool kDirect = !FP8 && (!PAGED || D <= 128);
+  // e4m3 from packed rows: K by direct loads (no widening), V through
+  // registers (widened to bf16 on the way).
+  static constexpr bool kDirectK = FP8 && !PAGED;
   static constexpr int kThreads = NW * kWave;
   // Wide heads on eight waves split D: waves w and w + kQGroups own the same 32
   // query rows (both compute its scores and softmax) and each keeps half of
@@ -153,11 +156,11 @@ struct KVStager {
 // chunk of a K/V row or a row's padding; padding lanes load from a parked
 // offset, which the range check turns into zeros.  Rows past the sequence
 // read as zeros (the descriptors end at its last key row).
-template <int D, int NW>
+template <int D, int NW, bool FP8 = false>
 struct DirectStager {
-  using G = Geom<D, false>;
+  using G = Geom<D, FP8>;
   static constexpr int kKSlots = G::kKRow / 16;  // slots per padded row = segments per stage
-  static constexpr int kVSlots = G::kVRow / 16;
+  static constexpr int kVSlots = G::kVRow / 16;  // (issue_v: bf16 only)
   static constexpr int kKPer = (kKSlots + NW - 1) / NW;  // segments per wave
   static constexpr int kVPer = (kVSlots + NW - 1) / NW;
   static_assert(G::kKRow % 16 == 0 && G::kVRow % 16 == 0, "padded rows must be whole slots");
@@ -505,7 +508,11 @@ void prefill_kernel(const PrefillParams p) {
     const int wv = uniform(wave);
     // The direct stager of this sequence's keys (packed rows or cache pages).
     auto make_direct = [&]() {
-      if constexpr (!C::kDirect) {
+      if constexpr (C::kDirectK) {
+        DirectStager<D, NW, true> st;  // K only
+        st.init(wv, lane, kr, vr, kv_row_bytes, kstart);
+        return st;
+      } else if constexpr (!C::kDirect) {
         return 0;  // staged through registers
       } else if constexpr (PAGED) {
         PagedDirectStager<D, NW, C::kKPage> st;
@@ -564,12 +571,8 @@ void prefill_kernel(const PrefillParams p) {
     if (lag) __syncthreads();
     const unsigned char* const sQw = sQ + (32 * qg) * G::kQRow;
     // bf16: the wave's Q^T operands move from the LDS tile to registers once.
-    u32x4 qop[FP8 ? 1 : D / 16];
-    if constexpr (!FP8) {
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-        qop[st] = lds_load16(sQw + (lane & 31) * G::kQRow, (uint32_t)((16 * st + 8 * h) * 2));
-    }
+    QOperands<D, FP8> qop;
+    if constexpr (!FP8) qop.load(sQw + (lane & 31) * G::kQRow, lane);
     auto fold_chunk = [&]() {
       float ca, cb;
       int mode;
@@ -600,7 +603,7 @@ void prefill_kernel(const PrefillParams p) {
         if constexpr (FP8) {
           qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + (j & 1) * C::kKStage, lane);
         } else {
-          qk_scores_qreg<D, C::kKPage>(s, qop, sK + (j & 1) * C::kKStage, lane);
+          qk_scores_qreg<D, FP8, C::kKPage>(s, qop, sK + (j & 1) * C::kKStage, lane);
         }
       }
       __syncthreads();
@@ -620,12 +623,15 @@ void prefill_kernel(const PrefillParams p) {
       } else {
     const int n = blk_end - blk_begin;
     KVStager<D, FP8, NW> rst;
+    // Register staging of block blk: K and V, or V alone where K is loaded
+    // directly (kDirectK); the direct K load of a block is issued before its V
+    // loads, so the wait for V covers it.
     auto reg_load = [&](int blk) {
       if constexpr (PAGED) {
         rst.load_paged(static_cast<const unsigned char*>(p.k), static_cast<const unsigned char*>(p.v),
                        blk * kBlockKeys, lk, p.token_stride, page_base, tid);
       } else {
-        rst.load(kr, blk * kBlockKeys - kstart, true, vr, blk * kBlockKeys - kstart, true,
+        rst.load(kr, blk * kBlockKeys - kstart, !C::kDirectK, vr, blk * kBlockKeys - kstart, true,
                  kv_row_bytes, tid);
       }
     };
@@ -635,6 +641,7 @@ void prefill_kernel(const PrefillParams p) {
       dst.issue_k(blk_begin, sK, wv);
       dst.issue_v(blk_begin, sV, wv);
     } else {
+      if constexpr (C::kDirectK) dst.issue_k(blk_begin, sK, wv);
       reg_load(blk_begin);
     }
     // Q tile -> LDS (rows past the sequence read as zero).
@@ -646,11 +653,16 @@ void prefill_kernel(const PrefillParams p) {
     if constexpr (C::kDirect) {
       wait_vm();
     } else {
-      rst.store(sK, true, sV, true, tid);
+      rst.store(sK, !C::kDirectK, sV, true, tid);
+      if constexpr (C::kDirectK) wait_vm();
     }
     __syncthreads();
 
     const unsigned char* const sQw = sQ + (32 * qg) * G::kQRow;  // this wave's Q rows
+    // e4m3 from packed rows (K staged directly, registers to spare): the
+    // wave's Q^T operands move from the LDS tile to registers once.
+    QOperands<D, FP8> qop;
+    if constexpr (C::kDirectK) qop.load(sQw + (lane & 31) * G::kQRow, lane);
     for (int j = 0; j < n; ++j) {
       const int blk = blk_begin + j, cur = j & 1;
       const bool more = j + 1 < n;
@@ -662,12 +674,17 @@ void prefill_kernel(const PrefillParams p) {
           dst.issue_k(blk + 1, sK + (cur ^ 1) * C::kKStage, wv);
           dst.issue_v(blk + 1, sV + (cur ^ 1) * C::kVStage, wv);
         } else {
+          if constexpr (C::kDirectK) dst.issue_k(blk + 1, sK + (cur ^ 1) * C::kKStage, wv);
           reg_load(blk + 1);
         }
       }
       if (wave_live(blk)) {
         f32x16 s[2];
-        qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + cur * C::kKStage, lane);
+        if constexpr (C::kDirectK) {
+          qk_scores_qreg<D, FP8, C::kKPage>(s, qop, sK + cur * C::kKStage, lane);
+        } else {
+          qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + cur * C::kKStage, lane);
+        }
         float alpha;
         u32x4 pb[4];
         softmax(blk, s, alpha, pb);
@@ -694,7 +711,9 @@ void prefill_kernel(const PrefillParams p) {
         if constexpr (C::kDirect) {
           wait_vm();
         } else {
-          rst.store(sK + (cur ^ 1) * C::kKStage, true, sV + (cur ^ 1) * C::kVStage, true, tid);
+          rst.store(sK + (cur ^ 1) * C::kKStage, !C::kDirectK, sV + (cur ^ 1) * C::kVStage, true,
+                    tid);
+          if constexpr (C::kDirectK) wait_vm();
         }
       }
       __syncthreads();
