@@ -202,3 +202,38 @@ def test_padded_rows_do_not_alias_next_sequence():
     assert_bitwise(out, ref, "sequences written one by one, last to first")
     alias = packed_alias_rows(lens, 128)
     assert sum(len(r) for r, _ in alias) == 60 + 127  # the predicted clobber set is non-empty
+
+
+@pytest.mark.parametrize("d", [64, 192])
+def test_e4m3_widening_every_code(d):
+    """A query that sees a single key returns that key's V row exactly (p = 1,
+    l = 1).  V rows holding all 256 E4M3FN codes pin the exact e4m3 -> bf16
+    widening of the V stage against the OCP decoding the oracle writes out
+    (NaN codes give NaN), through prefill and through the paged decode."""
+    import oracle
+    nrows = 256 // d + (1 if 256 % d else 0)
+    lens = [1] * nrows
+    inp = synth.prefill_inputs(61, lens, 1, 1, d, True, dtype="fp8")
+    codes = torch.arange(nrows * d, dtype=torch.int64) % 256
+    v = codes.to(torch.uint8).reshape(nrows, 1, d)
+    inp = synth.PrefillInputs(inp.q, inp.k, v, inp.cu_seqlens_q, inp.cu_seqlens_k, lens, lens, 1, 1,
+                              d, inp.scale, True, "fp8", inp.q_scale, inp.k_scale, 1.0, inp.seed)
+    # The accumulator starts at +0 and +0 + (-0) = +0, so the -0 code comes out as +0.
+    table = oracle.e4m3fn_table()[codes.numpy()] + 0.0
+    want = torch.from_numpy(table).to(torch.bfloat16).reshape(nrows, 1, d)
+    nan = torch.isnan(want)
+    assert nan.any() and not nan.all()
+    for sched in (MONO, SPLIT):
+        note(f"e4m3 widening d={d} schedule={sched}")
+        o = _prefill(inp, sched).cpu()
+        assert torch.isnan(o[nan]).all(), "NaN codes must widen to NaN"
+        assert_bitwise(o[~nan], want[~nan], f"prefill schedule {sched}")
+    kc = inp.k.reshape(nrows, 1, 1, d).expand(nrows, 16, 1, d).contiguous()
+    vc = v.reshape(nrows, 1, 1, d).expand(nrows, 16, 1, d).contiguous()
+    pages = torch.arange(nrows, dtype=torch.int32).reshape(nrows, 1)
+    dec = synth.DecodeInputs(inp.q.contiguous(), kc, vc, pages, torch.ones(nrows, dtype=torch.int32),
+                             1, 1, d, 16, inp.scale, 0, "fp8", inp.q_scale, inp.k_scale, 1.0)
+    for sched in (SPLIT, MONO):
+        o = run_decode(dec, sched).cpu().reshape(nrows, 1, d)
+        assert torch.isnan(o[nan]).all(), "NaN codes must widen to NaN"
+        assert_bitwise(o[~nan], want[~nan], f"decode schedule {sched}")
