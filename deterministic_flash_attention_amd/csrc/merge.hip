@@ -8,6 +8,11 @@
 // in registers, so both schedules produce the same bits.  A left fold is
 // required: fp32 addition is not associative, so a pairwise tree over chunks
 // would differ from the monolithic order.
+//
+// The loads are taken off the fold's critical path: lane c reads chunk c's
+// (m, l) for 64 chunks at once, a ballot names the non-empty ones, and their
+// accumulators are read kBatch at a time before the sequential fold over them
+// (skipping an empty partial is exactly the fold's own "keep" case).
 #include "contract.hpp"
 #include "kernels.hpp"
 
@@ -21,6 +26,7 @@ template <int D>
 __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergeParams p) {
   static_assert(D % 64 == 0, "one wave covers D in steps of 64 lanes");
   constexpr int PER = D / 64;
+  constexpr int kBatch = 8;  // accumulators in flight per wave
   const int lane = threadIdx.x & 63;
   const int64_t rh = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
   const int64_t nrh = p.rows * p.hq;
@@ -30,17 +36,48 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
   float A[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) A[k] = 0.0f;
-  for (int c = 0; c < p.cmax; ++c) {
-    const int64_t slot = (int64_t)c * nrh + rh;
-    const float m = p.part_ml[2 * slot];
-    const float l = p.part_ml[2 * slot + 1];
-    float ca, cb;
-    int mode;
-    merge_stats(M, L, m, l, ca, cb, mode);
-    if (mode != 0) {
-      const float* acc = p.part_acc + slot * D;
+  for (int c0 = 0; c0 < p.cmax; c0 += 64) {
+    // Lane c holds the (m, l) of chunk c0 + c; chunks past cmax read as empty.
+    float mc = -INFINITY, lc = 0.0f;
+    if (c0 + lane < p.cmax) {
+      const int64_t slot = (int64_t)(c0 + lane) * nrh + rh;
+      mc = p.part_ml[2 * slot];
+      lc = p.part_ml[2 * slot + 1];
+    }
+    uint64_t live = __builtin_amdgcn_ballot_w64(mc != -INFINITY);
+    while (live != 0) {
+      // The next (up to) kBatch non-empty chunks, ascending: read their
+      // accumulators, then fold them one by one.
+      int cs[kBatch];
+      float acc[kBatch][PER];
+      int nb = 0;
 #pragma unroll
-      for (int k = 0; k < PER; ++k) A[k] = merge_elem(A[k], acc[lane + 64 * k], mode, ca, cb);
+      for (int b = 0; b < kBatch; ++b) {
+        cs[b] = -1;
+        if (live != 0) {
+          const int c = (int)__builtin_ctzll(live);
+          live &= live - 1;
+          cs[b] = c;
+          nb = b + 1;
+          const float* ap = p.part_acc + ((int64_t)(c0 + c) * nrh + rh) * D;
+#pragma unroll
+          for (int k = 0; k < PER; ++k) acc[b][k] = ap[lane + 64 * k];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (b < nb) {
+          const float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                        __builtin_bit_cast(int, mc), cs[b]));
+          const float l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                        __builtin_bit_cast(int, lc), cs[b]));
+          float ca, cb;
+          int mode;
+          merge_stats(M, L, m, l, ca, cb, mode);
+#pragma unroll
+          for (int k = 0; k < PER; ++k) A[k] = merge_elem(A[k], acc[b][k], mode, ca, cb);
+        }
+      }
     }
   }
   uint16_t* o = static_cast<uint16_t*>(p.o) + rh * D;
