@@ -390,11 +390,23 @@ void prefill_kernel(const PrefillParams p) {
     lk = uniform(p.cu_k[b + 1]) - k_start;
   }
   if (lq <= 0 || q_start < 0 || k_start < 0) return;
-  const int ntiles = (lq + C::kTileRows - 1) / C::kTileRows;
+  // A single-token sequence over a paged cache (a decode row) packs the query
+  // heads of its kv head into one tile: row r is query head head + r at the
+  // sequence's one position, so the group's K/V stream once instead of once
+  // per query head.  Every row runs the arithmetic it runs alone (rows are
+  // independent), so the bits are those of the unpacked tiles.  The group's
+  // first head computes the tile; the others have nothing to do.
+  const int grp_size = p.hq / p.hkv;
+  const bool pack = PAGED && lq == 1 && grp_size > 1;
+  if (pack && head % grp_size != 0) return;
+  const int nrows = pack ? grp_size : lq;  // real rows of this tile set
+  const int64_t rs = pack ? 1 : p.hq;      // row stride in head rows
+  auto pos = [&](int i) { return pack ? 0 : i; };  // query position of local row i
+  const int ntiles = (nrows + C::kTileRows - 1) / C::kTileRows;
   const int tile = ntiles - 1 - tile_rev;
   if (tile < 0) return;
   const int r0 = tile * C::kTileRows;
-  const int g = head / (p.hq / p.hkv);
+  const int g = head / grp_size;
 
   // Visible keys of local query row i: [row_lo(i), row_hi(i)), bounds on the
   // bottom-right diagonal i + koff (causal, and a sliding window's left and
@@ -410,11 +422,11 @@ void prefill_kernel(const PrefillParams p) {
     return max(hi, 0);
   };
   // Key ranges of this tile's real rows.
-  const int last = min(r0 + C::kTileRows, lq) - 1;
-  const int kstart = row_lo(r0);    // first key visible to some row
-  const int kend = row_hi(last);    // past the last key visible to some row
-  const int klo_full = row_lo(last);  // keys in [klo_full, kfull) are visible to every row
-  const int kfull = row_hi(r0);
+  const int last = min(r0 + C::kTileRows, nrows) - 1;
+  const int kstart = row_lo(pos(r0));    // first key visible to some row
+  const int kend = row_hi(pos(last));    // past the last key visible to some row
+  const int klo_full = row_lo(pos(last));  // keys in [klo_full, kfull) are visible to every row
+  const int kfull = row_hi(pos(r0));
   const int nblk = kend > kstart ? (kend + kBlockKeys - 1) / kBlockKeys : 0;
   const int blk_first = kend > kstart ? kstart / kBlockKeys : 0;
   int blk_begin = blk_first, blk_end = nblk;
@@ -426,7 +438,7 @@ void prefill_kernel(const PrefillParams p) {
   // Query group (32 rows) and output columns [32 dt0, 32 (dt0 + NT)) of this wave.
   const int qg = wave % C::kQGroups, dt0 = (wave / C::kQGroups) * NT;
   const int qrow = r0 + 32 * qg + (lane & 31);  // local query row of this lane
-  const int lo = row_lo(qrow), hi = row_hi(qrow);
+  const int lo = row_lo(pos(qrow)), hi = row_hi(pos(qrow));
   // Blocks [wblk_first, wblk_end) hold a key visible to some row of this wave;
   // the others are fully masked for all of its rows (a wave whose rows all lie
   // past the sequence has none).  Such a block leaves m, l and acc exactly as
@@ -434,11 +446,11 @@ void prefill_kernel(const PrefillParams p) {
   // adding zero products changes no bit), so the wave skips its arithmetic
   // while still taking part in the staging and the barriers.
   const int wrow0 = r0 + 32 * ((int)uniform(wave) % C::kQGroups);
-  const int wrow_last = min(wrow0 + 31, lq - 1);
-  const bool wactive = wrow0 < lq;
-  const int wlo = wactive ? row_lo(wrow0) : 0;
-  const int wlo_max = wactive ? row_lo(wrow_last) : 0;  // a lower edge masks blocks below it
-  const int whi = wactive ? row_hi(wrow_last) : 0;
+  const int wrow_last = min(wrow0 + 31, nrows - 1);
+  const bool wactive = wrow0 < nrows;
+  const int wlo = wactive ? row_lo(pos(wrow0)) : 0;
+  const int wlo_max = wactive ? row_lo(pos(wrow_last)) : 0;  // a lower edge masks blocks below it
+  const int whi = wactive ? row_hi(pos(wrow_last)) : 0;
   const int wblk_first = wlo / kBlockKeys;
   const int wblk_end = whi > wlo ? (whi + kBlockKeys - 1) / kBlockKeys : 0;
   auto wave_live = [&](int blk) { return blk >= wblk_first && blk < wblk_end; };
@@ -448,9 +460,9 @@ void prefill_kernel(const PrefillParams p) {
       // Empty chunk for this tile: every row's partial is (m, l) = (-inf, 0).
       const int64_t ml_head = ((int64_t)chunk * p.total_q + q_start) * p.hq + head;
       const rsrc_t mlr = make_rsrc(p.part_ml + 2 * ml_head,
-                                   extent_bytes(lq, (int64_t)p.hq * 8, 8,
+                                   extent_bytes(nrows, rs * 8, 8,
                                                 ((int64_t)(chunk + 1) * p.total_q * p.hq - ml_head) * 8));
-      const uint32_t off = h ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 8);
+      const uint32_t off = h ? kParked : (uint32_t)qrow * (uint32_t)(rs * 8);
       buf_store8(mlr, off, u32x2{f32_bits(-INFINITY), 0u});
       return;
     }
@@ -483,12 +495,12 @@ void prefill_kernel(const PrefillParams p) {
   if (blk_begin < blk_end) {
     const int64_t q_head = (int64_t)q_start * p.hq + head;
     const int64_t kv_head = (int64_t)k_start * p.hkv + g;
-    const uint32_t q_row_bytes = (uint32_t)(p.hq * G::kRowBytes);
+    const uint32_t q_row_bytes = (uint32_t)(rs * G::kRowBytes);
     const uint32_t kv_row_bytes = (uint32_t)(p.hkv * G::kRowBytes);
     const unsigned char* qb = static_cast<const unsigned char*>(p.q) + q_head * G::kRowBytes;
     const unsigned char* kb = static_cast<const unsigned char*>(p.k) + kv_head * G::kRowBytes;
     const unsigned char* vb = static_cast<const unsigned char*>(p.v) + kv_head * G::kRowBytes;
-    const rsrc_t qr = make_rsrc(qb, extent_bytes(lq, q_row_bytes, G::kRowBytes,
+    const rsrc_t qr = make_rsrc(qb, extent_bytes(nrows, q_row_bytes, G::kRowBytes,
                                                  (p.total_q * p.hq - q_head) * G::kRowBytes));
     // Window-sized K/V descriptors: they cover key rows [kstart, kend) of the
     // sequence, the keys some row of this tile can see (aiter MQA-logits page:
@@ -724,15 +736,15 @@ void prefill_kernel(const PrefillParams p) {
   if constexpr (SPLIT) {
     const int64_t ml_head = ((int64_t)chunk * p.total_q + q_start) * p.hq + head;
     const rsrc_t mlr = make_rsrc(p.part_ml + 2 * ml_head,
-                                 extent_bytes(lq, (int64_t)p.hq * 8, 8,
+                                 extent_bytes(nrows, rs * 8, 8,
                                               ((int64_t)(chunk + 1) * p.total_q * p.hq - ml_head) * 8));
-    buf_store8(mlr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 8),
+    buf_store8(mlr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(rs * 8),
                u32x2{f32_bits(m), f32_bits(l)});
     const int64_t acc_head = ml_head * D;
     const rsrc_t ar = make_rsrc(p.part_acc + acc_head,
-                                extent_bytes(lq, (int64_t)p.hq * D * 4, D * 4,
+                                extent_bytes(nrows, rs * D * 4, D * 4,
                                              ((int64_t)(chunk + 1) * p.total_q * p.hq * D - acc_head) * 4));
-    const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(p.hq * D * 4);
+    const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(rs * D * 4);
 #pragma unroll
     for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -747,9 +759,9 @@ void prefill_kernel(const PrefillParams p) {
   } else {
     const int64_t o_head = (int64_t)q_start * p.hq + head;
     const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + o_head * D * 2,
-                                 extent_bytes(lq, (int64_t)p.hq * D * 2, D * 2,
+                                 extent_bytes(nrows, rs * D * 2, D * 2,
                                               (p.total_q * p.hq - o_head) * D * 2));
-    const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(p.hq * D * 2);
+    const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(rs * D * 2);
     const float vd = p.v_descale;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
@@ -763,9 +775,9 @@ void prefill_kernel(const PrefillParams p) {
         buf_store8(orr, rowoff + (uint32_t)d * 2u, u32x2{w0, w1});
       }
     if (p.lse != nullptr) {
-      const rsrc_t lr = make_rsrc(p.lse + o_head, extent_bytes(lq, (int64_t)p.hq * 4, 4,
+      const rsrc_t lr = make_rsrc(p.lse + o_head, extent_bytes(nrows, rs * 4, 4,
                                                                (p.total_q * p.hq - o_head) * 4));
-      buf_store4(lr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(p.hq * 4),
+      buf_store4(lr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(rs * 4),
                  f32_bits(finalize_lse(M, L)));
     }
   }
