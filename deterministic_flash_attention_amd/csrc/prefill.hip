@@ -606,9 +606,6 @@ void prefill_kernel(const PrefillParams p) {
       __builtin_amdgcn_s_setprio(2);  // MFMA phase ahead of the other half's VALU
       if (j > 0) {
         if (wave_live(blk - 1)) pv_mfma<D, NT>(acc, dt0, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
-        if constexpr (!SPLIT) {
-          if (blk % kBlocksPerChunk == 0) fold_chunk();
-        }
       }
       f32x16 s[2];
       if (live) {
@@ -617,6 +614,9 @@ void prefill_kernel(const PrefillParams p) {
         } else {
           qk_scores_qreg<D, FP8, C::kKPage>(s, qop, sK + (j & 1) * C::kKStage, lane);
         }
+      }
+      if constexpr (!SPLIT) {
+        if (j > 0 && blk % kBlocksPerChunk == 0) fold_chunk();
       }
       __syncthreads();
       __builtin_amdgcn_s_setprio(0);
