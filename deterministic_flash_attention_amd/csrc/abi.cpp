@@ -42,10 +42,11 @@ size_t partials_bytes_or_max(int64_t rows, int64_t hq, int64_t chunks, int64_t d
 int32_t gemm_chunks(int64_t k) { return k <= 0 ? 0 : (int32_t)((k + DG_CHUNK_K - 1) / DG_CHUNK_K); }
 
 // Tile shape when the caller leaves it open.  Every choice computes the same
-// bits.  The two large tiles want two workgroups per CU (512 launches or more):
-// 128 x 192 when N has no ragged 192-column tail, else 128 x 128.  Otherwise
-// the largest tile whose launch (tiles x split factor) still covers the 256
-// compute units, else the one with the most workgroups.
+// bits.  The large tiles want two waves per SIMD and 512 launches or more:
+// when N has no ragged 192-column tail, 256 x 192 (eight waves, one workgroup
+// per CU) or else 128 x 192 (four waves, two per CU); otherwise 128 x 128.
+// Smaller problems take the largest tile whose launch (tiles x split factor)
+// still covers the 256 compute units, else the one with the most workgroups.
 int64_t gemm_launch_count(int32_t cfg, int64_t m, int64_t n, int64_t split_factor) {
   int bm = 0, bn = 0;
   detattn::gemm_config_tile(cfg, &bm, &bn);
@@ -53,11 +54,12 @@ int64_t gemm_launch_count(int32_t cfg, int64_t m, int64_t n, int64_t split_facto
 }
 
 int32_t gemm_auto_config(int64_t m, int64_t n, int64_t split_factor) {
+  if (n % 192 == 0 && gemm_launch_count(5, m, n, split_factor) >= 512) return 5;
   if (n % 192 == 0 && gemm_launch_count(0, m, n, split_factor) >= 512) return 0;
   if (gemm_launch_count(1, m, n, split_factor) >= 512) return 1;
   int32_t best = 1;
   int64_t best_count = -1;
-  for (int32_t cfg = 1; cfg < detattn::gemm_num_configs(); ++cfg) {
+  for (int32_t cfg = 1; cfg <= 4; ++cfg) {
     const int64_t count = gemm_launch_count(cfg, m, n, split_factor);
     if (count >= 256) return cfg;
     if (count > best_count) {

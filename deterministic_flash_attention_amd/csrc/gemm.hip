@@ -105,8 +105,9 @@ __device__ __forceinline__ void barrier() {
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES, bool KN, bool SPLIT>
-// Two waves per SIMD: the large tiles run two workgroups per CU.
-__global__ __launch_bounds__(WM * WN * 64, 2) void gemm_kernel(const GemmParams p) {
+// Two waves per SIMD: four-wave tiles run two workgroups per CU, eight-wave
+// tiles one.
+__global__ __launch_bounds__(WM * WN * 64, WM * WN >= 8 ? 1 : 2) void gemm_kernel(const GemmParams p) {
   using C = GemmCfg<BM, BN, WM, WN, STAGES, KN>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::kLds];
 
@@ -379,10 +380,10 @@ hipError_t launch_cfg(const GemmParams& p0, bool kn, bool split, hipStream_t str
 // overlap the other's MFMAs; the small ones serve few rows (decode), where a
 // workgroup streams one chunk of the weight and more blocks in flight hide the
 // memory latency.
-int gemm_num_configs() { return 5; }
+int gemm_num_configs() { return 6; }
 
 void gemm_config_tile(int config, int* bm, int* bn) {
-  static const int kTiles[5][2] = {{128, 192}, {128, 128}, {64, 64}, {32, 64}, {32, 32}};
+  static const int kTiles[6][2] = {{128, 192}, {128, 128}, {64, 64}, {32, 64}, {32, 32}, {256, 192}};
   *bm = kTiles[config][0];
   *bn = kTiles[config][1];
 }
@@ -396,6 +397,7 @@ hipError_t launch_gemm(const GemmParams& p, int config, bool kn, bool split, hip
       case 2: e = launch_cfg<64, 64, 2, 2, 6>(p, kn, split, stream); break;
       case 3: e = launch_cfg<32, 64, 1, 2, 8>(p, kn, split, stream); break;
       case 4: e = launch_cfg<32, 32, 1, 1, 8>(p, kn, split, stream); break;
+      case 5: e = launch_cfg<256, 192, 4, 2, 2>(p, kn, split, stream); break;
       default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess || !split) return e;
