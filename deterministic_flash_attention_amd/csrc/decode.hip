@@ -33,9 +33,12 @@ struct DecodeCfg {
   static constexpr int kBlockChunks = kBlockKeys * G::kChunks16;
   static constexpr int kPerThread = kBlockChunks / kThreads;
   static_assert(kPerThread * kThreads == kBlockChunks, "K/V chunks must split evenly");
+  // One K and one V stage: a workgroup's next block waits in registers, and
+  // the small footprint lets four (bf16) or five (e4m3) workgroups share a CU,
+  // whose interleaving hides the load latency better than a second stage.
   static constexpr int kKOff = 0;
-  static constexpr int kVOff = 2 * G::kKStage;
-  static constexpr int kLds = kVOff + 2 * G::kVStage;
+  static constexpr int kVOff = G::kKStage;
+  static constexpr int kLds = kVOff + G::kVStage;
   static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
@@ -209,11 +212,10 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
     for (int blk = blk_begin; blk < blk_end;) {
       const int cend = min(blk_end, (blk / kBlocksPerChunk + 1) * kBlocksPerChunk);
       for (; blk < cend; ++blk) {
-        const int cur = (blk - blk_begin) & 1;
         const bool more = blk + 1 < blk_end;
         if (more) stg.load(kc, vc, (blk + 1) * kBlockKeys, ctx, p.token_stride, tid, page_base);
-        const unsigned char* ks = sK + cur * G::kKStage;
-        const unsigned char* vs = sV + cur * G::kVStage;
+        const unsigned char* ks = sK;
+        const unsigned char* vs = sV;
         f32x16 s[2];
         qk_scores_qrow<D, FP8>(s, qrow, ks, lane);
         float alpha;
@@ -227,8 +229,9 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
           softmax_block<kMaskLoHi>(s, h, c, lo - b0, ctx - b0, m, l, alpha, pb);
         }
         pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
-        if (more) stg.store(sK + (cur ^ 1) * G::kKStage, sV + (cur ^ 1) * G::kVStage, tid);
-        __syncthreads();
+        __syncthreads();  // every wave is done with the stage
+        if (more) stg.store(sK, sV, tid);
+        __syncthreads();  // block blk+1 is staged
       }
       const int chunk = (blk - 1) / kBlocksPerChunk;  // the chunk just completed
       if constexpr (SPLIT) {
