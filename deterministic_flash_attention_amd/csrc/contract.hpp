@@ -315,24 +315,21 @@ __device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[NT], int dt0, float 
 }
 
 // Chunk merge: fold one partial (m, l) into the running (M, L).
-// mode 0: partial empty, keep; 1: total empty, copy; 2: rescale with (ca, cb).
+// keep: the partial is empty (m = -inf) and the total stays as it is.
+// Otherwise each side is scaled by exp2 of its max minus the new max, and an
+// empty total gets coefficient 0 instead (its A and L are +0, so the fold then
+// copies the partial); the new element is fma(A, ca, acc * cb), two roundings.
 __device__ __forceinline__ void merge_stats(float& M, float& L, float m, float l, float& ca,
-                                            float& cb, int& mode) {
-  const bool part_empty = (m == -INFINITY);
-  const bool tot_empty = (M == -INFINITY);
+                                            float& cb, bool& keep) {
+  keep = (m == -INFINITY);
   const float Mn = fmaxf(M, m);
-  const float a = __builtin_amdgcn_exp2f(M - Mn);
-  const float b = __builtin_amdgcn_exp2f(m - Mn);
-  mode = part_empty ? 0 : (tot_empty ? 1 : 2);
-  ca = a;
-  cb = b;
-  const float Lr = L * a + l * b;
-  L = (mode == 0) ? L : ((mode == 1) ? l : Lr);
-  M = (mode == 0) ? M : ((mode == 1) ? m : Mn);
+  ca = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
+  cb = __builtin_amdgcn_exp2f(m - Mn);
+  L = keep ? L : __builtin_fmaf(L, ca, l * cb);
+  M = Mn;
 }
-__device__ __forceinline__ float merge_elem(float A, float acc, int mode, float ca, float cb) {
-  const float r = A * ca + acc * cb;
-  return (mode == 0) ? A : ((mode == 1) ? acc : r);
+__device__ __forceinline__ float merge_elem(float A, float acc, bool keep, float ca, float cb) {
+  return keep ? A : __builtin_fmaf(A, ca, acc * cb);
 }
 
 __device__ __forceinline__ float finalize_elem(float A, float L, float v_descale) {

@@ -247,10 +247,10 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
         }
       } else {
         float ca, cb;
-        int mode;
-        merge_stats(M, L, m, l, ca, cb, mode);
+        bool keep;
+        merge_stats(M, L, m, l, ca, cb, keep);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) A[0][i] = merge_elem(A[0][i], acc[0][i], mode, ca, cb);
+        for (int i = 0; i < 16; ++i) A[0][i] = merge_elem(A[0][i], acc[0][i], keep, ca, cb);
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[0][i] = 0.0f;

@@ -72,10 +72,10 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
           const float l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                         __builtin_bit_cast(int, lc), cs[b]));
           float ca, cb;
-          int mode;
-          merge_stats(M, L, m, l, ca, cb, mode);
+          bool keep;
+          merge_stats(M, L, m, l, ca, cb, keep);
 #pragma unroll
-          for (int k = 0; k < PER; ++k) A[k] = merge_elem(A[k], acc[b][k], mode, ca, cb);
+          for (int k = 0; k < PER; ++k) A[k] = merge_elem(A[k], acc[b][k], keep, ca, cb);
         }
       }
     }

@@ -587,13 +587,13 @@ void prefill_kernel(const PrefillParams p) {
     if constexpr (!FP8) qop.load(sQw + (lane & 31) * G::kQRow, lane);
     auto fold_chunk = [&]() {
       float ca, cb;
-      int mode;
-      merge_stats(M, L, m, l, ca, cb, mode);
+      bool keep;
+      merge_stats(M, L, m, l, ca, cb, keep);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          A[t][i] = merge_elem(A[t][i], acc[t][i], mode, ca, cb);
+          A[t][i] = merge_elem(A[t][i], acc[t][i], keep, ca, cb);
           acc[t][i] = 0.0f;
         }
       m = -INFINITY;
@@ -706,13 +706,13 @@ void prefill_kernel(const PrefillParams p) {
         if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) {
           // End of a 512-key chunk: fold its partial into the running total.
           float ca, cb;
-          int mode;
-          merge_stats(M, L, m, l, ca, cb, mode);
+          bool keep;
+          merge_stats(M, L, m, l, ca, cb, keep);
 #pragma unroll
           for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              A[t][i] = merge_elem(A[t][i], acc[t][i], mode, ca, cb);
+              A[t][i] = merge_elem(A[t][i], acc[t][i], keep, ca, cb);
               acc[t][i] = 0.0f;
             }
           m = -INFINITY;
