@@ -9,11 +9,13 @@
 // can check that the two schedules agree bit for bit.
 //
 // The query heads of one group occupy columns 0..G-1 of the 32-column MFMA
-// tile; the remaining columns carry zero queries and are never stored.  Every
-// wave computes the (identical) scores and softmax for all columns and owns one
-// 32-wide slice of the output, so D/32 waves share the K/V traffic of a block.
-// The per-block arithmetic is the one in contract.hpp, which makes a decode row
-// bitwise equal to the last row of the prefill of the same sequence.
+// tile; the remaining columns carry zero queries and are never stored.  The
+// scores and softmax of a block are computed once, by one wave (the role
+// rotates over the D/32 waves block by block, so every SIMD gets its share),
+// which publishes P^T and (alpha, m, l) through LDS; every wave then applies
+// them to its own 32-wide slice of the output.  The per-block arithmetic is the
+// one in contract.hpp on the same operands, which makes a decode row bitwise
+// equal to the last row of the prefill of the same sequence.
 #include "contract.hpp"
 #include "kernels.hpp"
 
@@ -34,11 +36,15 @@ struct DecodeCfg {
   static constexpr int kPerThread = kBlockChunks / kThreads;
   static_assert(kPerThread * kThreads == kBlockChunks, "K/V chunks must split evenly");
   // One K and one V stage: a workgroup's next block waits in registers, and
-  // the small footprint lets four (bf16) or five (e4m3) workgroups share a CU,
-  // whose interleaving hides the load latency better than a second stage.
+  // the small footprint lets several workgroups share a CU, whose
+  // interleaving hides the load latency better than a second stage.  The P
+  // slot holds the block's P^T operands (four 1 KB rows of 16 bytes per lane)
+  // and one row of (alpha, m, l) per lane.
   static constexpr int kKOff = 0;
   static constexpr int kVOff = G::kKStage;
-  static constexpr int kLds = kVOff + G::kVStage;
+  static constexpr int kPOff = kVOff + G::kVStage;
+  static constexpr int kPRow = kWave * 16;
+  static constexpr int kLds = kPOff + 5 * kPRow;
   static_assert(kLds <= 160 * 1024, "LDS budget");
 };
 
@@ -57,31 +63,41 @@ struct PagedStager {
   __device__ __forceinline__ void load(const unsigned char* kc, const unsigned char* vc, int key0,
                                        int ctx, int64_t token_stride, int tid,
                                        const PageBase& page_base) {
+    int64_t off[C::kPerThread];  // byte offset of each chunk in the cache, or -1
 #pragma unroll
     for (int u = 0; u < C::kPerThread; ++u) {
       const int x = tid + u * C::kThreads;
       const int r = x / G::kChunks16, col = x % G::kChunks16;
       const int j = key0 + r;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      int64_t byte = -1;
       if (j < ctx) {
         const int64_t base = page_base(j);
-        if (base >= 0) {
-          const int64_t e = base + (int64_t)(j % kPageSize) * token_stride;
-          const int64_t byte = e * G::kEs + (int64_t)col * 16;
-          kv = *reinterpret_cast<const u32x4*>(kc + byte);
-          vv = *reinterpret_cast<const u32x4*>(vc + byte);
-        }
+        if (base >= 0) byte = (base + (int64_t)(j % kPageSize) * token_stride) * G::kEs + col * 16;
       }
-      kreg[u] = kv;
-      vreg[u] = vv;
+      off[u] = byte;
     }
+    // All K loads are issued before the V loads, so the K stage can be
+    // written while the V loads are still in flight.
+#pragma unroll
+    for (int u = 0; u < C::kPerThread; ++u)
+      kreg[u] = off[u] >= 0 ? *reinterpret_cast<const u32x4*>(kc + off[u]) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < C::kPerThread; ++u)
+      vreg[u] = off[u] >= 0 ? *reinterpret_cast<const u32x4*>(vc + off[u]) : u32x4{0u, 0u, 0u, 0u};
   }
-  __device__ __forceinline__ void store(unsigned char* ks, unsigned char* vs, int tid) const {
+  __device__ __forceinline__ void store_k(unsigned char* ks, int tid) const {
 #pragma unroll
     for (int u = 0; u < C::kPerThread; ++u) {
       const int x = tid + u * C::kThreads;
       const int r = x / G::kChunks16, col = x % G::kChunks16;
       lds_store16(ks, (uint32_t)(r * G::kKRow + col * 16), kreg[u]);
+    }
+  }
+  __device__ __forceinline__ void store_v(unsigned char* vs, int tid) const {
+#pragma unroll
+    for (int u = 0; u < C::kPerThread; ++u) {
+      const int x = tid + u * C::kThreads;
+      const int r = x / G::kChunks16, col = x % G::kChunks16;
       if constexpr (FP8) {
         const u32x2 a = e4m3x4_to_bf16x4(vreg[u][0]), b = e4m3x4_to_bf16x4(vreg[u][1]);
         const u32x2 c = e4m3x4_to_bf16x4(vreg[u][2]), d = e4m3x4_to_bf16x4(vreg[u][3]);
@@ -105,6 +121,7 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
   extern __shared__ __attribute__((aligned(16))) unsigned char sQ[];
   unsigned char* const sK = smem + C::kKOff;
   unsigned char* const sV = smem + C::kVOff;
+  unsigned char* const sP = smem + C::kPOff;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, n = lane & 31;
@@ -205,33 +222,57 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
         return lookup(j / kPageSize);
       }
     };
+    // Block pipeline: the K and V of block blk sit in the LDS stages and those
+    // of blk+1 in registers.  (1) The block's score wave computes S and the
+    // softmax and publishes P^T, alpha, m and l in the P slot; barrier.
+    // (2) Every wave takes them, stores K(blk+1) into the K stage (the
+    // scores of blk are done) and adds P V to its output slice; barrier.
+    // (3) Every wave stores V(blk+1) into the V stage and issues the loads of
+    // blk+2.  The barrier of (1) in the next block publishes that V stage.
     PagedStager<D, FP8> stg;
     stg.load(kc, vc, blk_begin * kBlockKeys, ctx, p.token_stride, tid, page_base);
-    stg.store(sK, sV, tid);
+    stg.store_k(sK, tid);
+    stg.store_v(sV, tid);
+    if (blk_begin + 1 < blk_end)
+      stg.load(kc, vc, (blk_begin + 1) * kBlockKeys, ctx, p.token_stride, tid, page_base);
     __syncthreads();
     for (int blk = blk_begin; blk < blk_end;) {
       const int cend = min(blk_end, (blk / kBlocksPerChunk + 1) * kBlocksPerChunk);
       for (; blk < cend; ++blk) {
         const bool more = blk + 1 < blk_end;
-        if (more) stg.load(kc, vc, (blk + 1) * kBlockKeys, ctx, p.token_stride, tid, page_base);
-        const unsigned char* ks = sK;
-        const unsigned char* vs = sV;
-        f32x16 s[2];
-        qk_scores_qrow<D, FP8>(s, qrow, ks, lane);
-        float alpha;
-        u32x4 pb[4];
-        const int b0 = kBlockKeys * blk;
-        if (b0 >= lo && b0 + kBlockKeys <= ctx) {
-          softmax_block<kNoMask>(s, h, c, 0, 0, m, l, alpha, pb);
-        } else if (b0 >= lo) {
-          softmax_block<kMaskHi>(s, h, c, 0, ctx - b0, m, l, alpha, pb);
-        } else {
-          softmax_block<kMaskLoHi>(s, h, c, lo - b0, ctx - b0, m, l, alpha, pb);
+        if (wave == blk % C::kWaves) {
+          f32x16 s[2];
+          qk_scores_qrow<D, FP8>(s, qrow, sK, lane);
+          float alpha;
+          u32x4 pb[4];
+          const int b0 = kBlockKeys * blk;
+          if (b0 >= lo && b0 + kBlockKeys <= ctx) {
+            softmax_block<kNoMask>(s, h, c, 0, 0, m, l, alpha, pb);
+          } else if (b0 >= lo) {
+            softmax_block<kMaskHi>(s, h, c, 0, ctx - b0, m, l, alpha, pb);
+          } else {
+            softmax_block<kMaskLoHi>(s, h, c, lo - b0, ctx - b0, m, l, alpha, pb);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) lds_store16(sP, (uint32_t)(k * C::kPRow + lane * 16), pb[k]);
+          lds_store16(sP, (uint32_t)(4 * C::kPRow + lane * 16),
+                      u32x4{f32_bits(alpha), f32_bits(m), f32_bits(l), 0u});
         }
-        pv_accumulate<D, 1>(acc, wave, alpha, pb, vs, lane);
-        __syncthreads();  // every wave is done with the stage
-        if (more) stg.store(sK, sV, tid);
-        __syncthreads();  // block blk+1 is staged
+        __syncthreads();  // P^T and the statistics of blk are published
+        u32x4 pb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) pb[k] = lds_load16(sP, (uint32_t)(k * C::kPRow + lane * 16));
+        const u32x4 st = lds_load16(sP, (uint32_t)(4 * C::kPRow + lane * 16));
+        m = bits_f32(st[1]);
+        l = bits_f32(st[2]);
+        if (more) stg.store_k(sK, tid);
+        pv_accumulate<D, 1>(acc, wave, bits_f32(st[0]), pb, sV, lane);
+        __syncthreads();  // every wave is done with the P slot and the V stage
+        if (more) {
+          stg.store_v(sV, tid);
+          if (blk + 2 < blk_end)
+            stg.load(kc, vc, (blk + 2) * kBlockKeys, ctx, p.token_stride, tid, page_base);
+        }
       }
       const int chunk = (blk - 1) / kBlocksPerChunk;  // the chunk just completed
       if constexpr (SPLIT) {
