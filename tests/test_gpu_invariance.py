@@ -50,13 +50,15 @@ def test_split_equals_monolithic_decode(dtype):
     assert_bitwise(l1, l2, "decode lse split vs monolithic")
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("bf16", 192), ("fp8", 192),
-                                     ("fp8", 128), ("fp8", 64)])
-def test_decode_equals_last_prefill_row(dtype, d):
+@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 8, 2), ("bf16", 64, 8, 2),
+                                            ("bf16", 192, 8, 2), ("fp8", 192, 8, 2),
+                                            ("fp8", 128, 8, 2), ("fp8", 64, 8, 2),
+                                            ("bf16", 128, 32, 1), ("fp8", 128, 4, 4)])
+def test_decode_equals_last_prefill_row(dtype, d, hq, hkv):
     """The decode token of a sequence of length L equals row L-1 of its causal
-    prefill, bit for bit, for lengths around block and chunk boundaries."""
+    prefill, bit for bit, for lengths around block and chunk boundaries (groups
+    of 4, of 32 query heads per kv head, and of one)."""
     lens = [1, 2, 63, 64, 65, 511, 512, 513, 1000, 1537]
-    hq, hkv = 8, 2
     inp = synth.prefill_inputs(35, lens, hq, hkv, d, True, dtype=dtype)
     o_pre = _prefill(inp, MONO)
     # Page the same K/V into a shuffled paged cache; the decode query is the last row.

@@ -118,6 +118,18 @@ def test_decode_gqa_group_2_head_dim_64():
     _decode_case([5, 700, 1025], 4, 2, 64, 23, SPLIT)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (16, 2), (32, 1)])
+def test_decode_group_sizes(hq, hkv, dtype):
+    """One, eight and 32 query heads per kv head (32: every column of the MFMA
+    tile is a query and none reads the zero row), against the oracle, with the
+    two schedules equal bit for bit."""
+    ctx = [1, 64, 513, 1100]
+    _, o_split = _decode_case(ctx, hq, hkv, 128, 29, SPLIT, dtype=dtype)
+    _, o_mono = _decode_case(ctx, hq, hkv, 128, 29, MONO, dtype=dtype)
+    assert torch.equal(o_split.view(torch.int16), o_mono.view(torch.int16)), "split != monolithic"
+
+
 def test_decode_fp8():
     _decode_case([3, 600, 1700], 8, 2, 128, 25, SPLIT, dtype="fp8")
 
