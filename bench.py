@@ -218,7 +218,7 @@ def decode_entry(iters, warmup, dtype="bf16"):
         "partials_bytes_written": part_bytes,
         "roofline": {"bound": "hbm", "achieved": gbs_split, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs_split / PEAK_HBM_GBS,
-                     "traffic": counted_traffic("decode_split_bf16") if dtype == "bf16" else None,
+                     "traffic": counted_traffic(f"decode_split_{dtype}"),
                      "kernel": "decode split"},
         "step_frac_of_hbm": gbs_step / PEAK_HBM_GBS,
     }
@@ -351,6 +351,7 @@ def pmc_pass():
     fn, _ = run_prefill_fn(inp, t, dfa.MONOLITHIC)
     fn()
     decode_entry(1, 0)
+    decode_entry(1, 0, dtype="fp8")
     for name, m, n, k in synth.GEMM_SHAPES:
         inp_g = synth.gemm_inputs(0, m, n, k)
         dfa.gemm(inp_g.a.cuda(), inp_g.w.cuda())
