@@ -428,3 +428,105 @@ def test_planted_e4m3_bias(monkeypatch):
     bad = t * 2.0  # an exponent bias of 6 instead of 7
     monkeypatch.setattr(oracle, "e4m3fn_table", lambda: bad)
     assert _fails(test_e4m3fn_table_spec_values)
+
+
+# ---------------------------------------------------------------------------
+# E4M3FN dequantisation: decode(code) * per-tensor scale.  Every fp8 parity
+# claim compares the GPU against the oracle on these values (ffpa-attn fp8
+# D=192 page, "Verification": errors are taken against the dequantised inputs).
+# ---------------------------------------------------------------------------
+DEQ_SCALES = [1.0, 0.0123, 3.75, 2.0 ** -7]
+
+
+@pytest.mark.parametrize("s", DEQ_SCALES)
+def test_dequantize_e4m3_closed_forms(s):
+    """Spec values of the OCP E4M3FN format times the scale, through the
+    function the parity tests call (not the table)."""
+    deq = oatt.dequantize_e4m3
+    codes = np.array([0x38, 0x7E, 0xFE, 0x01, 0x08, 0x00, 0x80, 0xB8, 0x40, 0x30, 0x7F, 0xFF],
+                     dtype=np.uint8)
+    want = [1.0, 448.0, -448.0, 2.0 ** -9, 2.0 ** -6, 0.0, -0.0, -1.0, 2.0, 0.5]
+    got = deq(codes, s)
+    for c, w, g in zip(codes, want, got):
+        assert g == w * s, f"code {c:#04x}: {g} != {w} * {s}"
+    assert math.copysign(1.0, got[6]) == -1.0
+    assert math.isnan(got[10]) and math.isnan(got[11])
+    # shape is kept and every element is decoded independently
+    grid = np.array([[0x38, 0x7E], [0x01, 0xB8]], dtype=np.uint8).reshape(2, 1, 2)
+    np.testing.assert_array_equal(deq(grid, s), np.array([[[s, 448.0 * s]], [[2.0 ** -9 * s, -s]]]))
+
+
+def test_dequantize_e4m3_matches_torch_decoder():
+    """All 256 codes against torch's float8_e4m3fn conversion (an independent
+    decoder of the same format), at several scales: decode exactly, then one
+    fp64 multiply by the scale."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for s in DEQ_SCALES:
+        got = oatt.dequantize_e4m3(codes, s)
+        np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+        fin = ~np.isnan(ref)
+        np.testing.assert_array_equal(got[fin], ref[fin] * np.float64(s))
+
+
+def test_dequantize_inverts_per_tensor_quantisation():
+    """Quantising x with the per-tensor amax/448 scale and dequantising gives x
+    back within half an E4M3 step: relative 2^-4 for normal codes, absolute
+    2^-10 * s below the smallest normal (2^-6 * s)."""
+    import torch
+    import synth
+    x = torch.randn(4096, generator=torch.Generator().manual_seed(5)) * 3.0
+    fq = synth.quantize_e4m3(x)
+    back = oatt.dequantize_e4m3(fq.codes.numpy(), fq.scale)
+    xs = x.double().numpy()
+    s = fq.scale
+    normal = np.abs(xs) >= 2.0 ** -6 * s
+    assert normal.sum() > 3000 and (~normal).sum() > 0
+    assert np.all(np.abs(back[normal] - xs[normal]) <= 2.0 ** -4 * np.abs(xs[normal]))
+    assert np.all(np.abs(back[~normal] - xs[~normal]) <= 2.0 ** -10 * s * (1 + 1e-12))
+    assert abs(np.abs(back).max() - np.abs(xs).max()) <= 2.0 ** -4 * np.abs(xs).max()
+
+
+def _deq_pins():
+    for s in DEQ_SCALES:
+        test_dequantize_e4m3_closed_forms(s)
+    test_dequantize_e4m3_matches_torch_decoder()
+    test_dequantize_inverts_per_tensor_quantisation()
+
+
+def test_planted_dequantize_divides_by_scale(monkeypatch):
+    monkeypatch.setattr(oatt, "dequantize_e4m3",
+                        lambda codes, scale: oatt._E4M3[np.asarray(codes, dtype=np.uint8)]
+                        / np.float64(scale))
+    assert _fails(_deq_pins)
+    assert _fails(test_dequantize_inverts_per_tensor_quantisation)
+
+
+def test_planted_dequantize_scales_code_before_decoding(monkeypatch):
+    def scaled_first(codes, scale):
+        c = np.asarray(codes, dtype=np.float64) * np.float64(scale)
+        return oatt._E4M3[np.rint(c).astype(np.int64) % 256]
+    monkeypatch.setattr(oatt, "dequantize_e4m3", scaled_first)
+    assert _fails(lambda: test_dequantize_e4m3_closed_forms(0.0123))
+    assert _fails(test_dequantize_e4m3_matches_torch_decoder)
+
+
+def test_planted_dequantize_table_bias(monkeypatch):
+    """A wrong exponent bias in the table dequantize_e4m3 actually reads."""
+    monkeypatch.setattr(oatt, "_E4M3", oatt.e4m3fn_table() * 2.0)
+    assert _fails(lambda: test_dequantize_e4m3_closed_forms(1.0))
+    assert _fails(test_dequantize_e4m3_matches_torch_decoder)
+    assert _fails(test_dequantize_inverts_per_tensor_quantisation)
+
+
+def test_planted_dequantize_subnormal_slip(monkeypatch):
+    """Subnormals decoded with the normal formula's implicit 1."""
+    bad = oatt.e4m3fn_table().copy()
+    for code in range(256):
+        if (code >> 3) & 0xF == 0 and code & 0x7:
+            sign = -1.0 if code & 0x80 else 1.0
+            bad[code] = sign * (1.0 + (code & 7) / 8.0) * 2.0 ** -6
+    monkeypatch.setattr(oatt, "_E4M3", bad)
+    assert _fails(lambda: test_dequantize_e4m3_closed_forms(1.0))
+    assert _fails(test_dequantize_e4m3_matches_torch_decoder)
