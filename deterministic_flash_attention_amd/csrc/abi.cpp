@@ -240,18 +240,21 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
   return e == hipSuccess ? DA_OK : DA_ELAUNCH;
 }
 
-da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cache,
-                                const void* v_cache, int64_t num_pages, int64_t page_stride,
-                                int64_t token_stride, int64_t head_stride,
-                                const int32_t* page_table, int32_t max_pages_per_seq,
-                                const int32_t* context_lens, int32_t max_context_len,
-                                int32_t window_left, int32_t batch, int32_t page_size,
-                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
-                                float softmax_scale, float q_descale, float k_descale,
-                                float v_descale, int32_t schedule, float* partials,
-                                size_t partials_bytes, void* o, float* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and parameters shared by the paged decode entry points.  Runs no
+// HIP call.  *cmax receives the chunk count of the split schedule.
+da_status decode_setup(int32_t dtype, const void* q, const void* k_cache, const void* v_cache,
+                       int64_t num_pages, int64_t page_stride, int64_t token_stride,
+                       int64_t head_stride, const int32_t* page_table, int32_t max_pages_per_seq,
+                       const int32_t* context_lens, int32_t max_context_len, int32_t window_left,
+                       int32_t batch, int32_t page_size, int32_t num_heads_q,
+                       int32_t num_heads_kv, int32_t head_dim, float softmax_scale,
+                       float q_descale, float k_descale, float v_descale, bool split,
+                       detattn::DecodeParams* out, int32_t* cmax_out) {
   if (dtype != DA_BF16 && dtype != DA_FP8_E4M3) return DA_EINVAL;
-  if (schedule != DA_MONOLITHIC && schedule != DA_SPLIT) return DA_EINVAL;
   if (window_left < -1) return DA_EINVAL;
   if (batch < 0 || max_context_len < 0 || max_pages_per_seq <= 0 || num_pages <= 0) return DA_EINVAL;
   if (page_stride <= 0 || token_stride <= 0 || head_stride <= 0) return DA_EINVAL;
@@ -262,31 +265,22 @@ da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cach
   if ((int64_t)max_context_len > (int64_t)max_pages_per_seq * DA_PAGE_SIZE) return DA_EINVAL;
   if (!finite_pos(softmax_scale)) return DA_EINVAL;
   if (!check_descales(dtype, q_descale, k_descale, v_descale)) return DA_EINVAL;
-  const bool split = schedule == DA_SPLIT;
   const int es = dtype == DA_FP8_E4M3 ? 1 : 2;
   if (!q || !k_cache || !v_cache || !page_table || !context_lens) return DA_EINVAL;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(page_table, 4) || !aligned(context_lens, 4))
     return DA_EINVAL;
   if ((page_stride * es) % 16 || (token_stride * es) % 16 || (head_stride * es) % 16) return DA_EINVAL;
-  if (!split && (!o || !aligned(o, 16) || (lse && !aligned(lse, 4)))) return DA_EINVAL;
-  if (split && (!partials || !aligned(partials, 16))) return DA_EINVAL;
   const int32_t cmax = chunks_for(max_context_len);
   if ((int64_t)batch * num_heads_kv * (split ? cmax : 1) > kMaxOffset) return DA_EUNSUPPORTED;
-  if (split && partials_bytes < partials_bytes_or_max(batch, num_heads_q, cmax, head_dim))
-    return DA_EWORKSPACE;
-  if (batch == 0 || (split && cmax == 0)) return DA_OK;
 
-  detattn::DecodeParams p{};
+  detattn::DecodeParams& p = *out;
+  p = detattn::DecodeParams{};
   p.q = q;
   p.kc = k_cache;
   p.vc = v_cache;
   p.page_table = page_table;
   p.ctx_lens = context_lens;
-  p.o = o;
-  p.lse = lse;
-  p.part_acc = partials;
-  p.part_ml = partials ? partials + (size_t)cmax * batch * num_heads_q * head_dim : nullptr;
   p.num_pages = num_pages;
   p.page_stride = page_stride;
   p.token_stride = token_stride;
@@ -300,6 +294,43 @@ da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cach
   p.window_left = window_left;
   p.c_scale = score_constant(softmax_scale, q_descale, k_descale);
   p.v_descale = v_descale;
+  *cmax_out = cmax;
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cache,
+                                const void* v_cache, int64_t num_pages, int64_t page_stride,
+                                int64_t token_stride, int64_t head_stride,
+                                const int32_t* page_table, int32_t max_pages_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len,
+                                int32_t window_left, int32_t batch, int32_t page_size,
+                                int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                float softmax_scale, float q_descale, float k_descale,
+                                float v_descale, int32_t schedule, float* partials,
+                                size_t partials_bytes, void* o, float* lse, void* stream) {
+  if (schedule != DA_MONOLITHIC && schedule != DA_SPLIT) return DA_EINVAL;
+  const bool split = schedule == DA_SPLIT;
+  detattn::DecodeParams p{};
+  int32_t cmax = 0;
+  const da_status st = decode_setup(dtype, q, k_cache, v_cache, num_pages, page_stride,
+                                    token_stride, head_stride, page_table, max_pages_per_seq,
+                                    context_lens, max_context_len, window_left, batch, page_size,
+                                    num_heads_q, num_heads_kv, head_dim, softmax_scale, q_descale,
+                                    k_descale, v_descale, split, &p, &cmax);
+  if (st != DA_OK) return st;
+  if (!split && (!o || !aligned(o, 16) || (lse && !aligned(lse, 4)))) return DA_EINVAL;
+  if (split && (!partials || !aligned(partials, 16))) return DA_EINVAL;
+  if (split && partials_bytes < partials_bytes_or_max(batch, num_heads_q, cmax, head_dim))
+    return DA_EWORKSPACE;
+  if (batch == 0 || (split && cmax == 0)) return DA_OK;
+  p.o = o;
+  p.lse = lse;
+  p.part_acc = partials;
+  p.part_ml = partials ? partials + (size_t)cmax * batch * num_heads_q * head_dim : nullptr;
   const hipError_t e = detattn::launch_decode(p, head_dim, dtype == DA_FP8_E4M3, split,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ELAUNCH;
@@ -379,7 +410,9 @@ da_status det_gemm_fwd(const void* a, int64_t lda, const void* w, int64_t ldw,
   det_gemm_config_tile(config, &bm, &bn);
   // Every byte offset inside one tile's descriptor must stay below 2^31.
   const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn);
-  if (tiles > kMaxOffset || m * (n / 4) / 256 > kMaxOffset) return DA_EUNSUPPORTED;
+  // Grid sizes: the tile grid, and the combine pass's one workgroup per 1024
+  // columns of a row.
+  if (tiles > kMaxOffset || m * ((n + 1023) / 1024) > kMaxOffset) return DA_EUNSUPPORTED;
   if (k > 0) {
     if (((bm - 1) * lda + k) * 2 > kMaxOffset) return DA_EUNSUPPORTED;
     if (kn ? (k * ldw + bn) * 2 > kMaxOffset : ((bn - 1) * ldw + k) * 2 > kMaxOffset)

@@ -29,11 +29,23 @@
 //     chunk order with the exact max/sum rescale (a skipped empty partial, a
 //     copy into an empty total, or M' = max(M, m_c), a = exp2(M - M'),
 //     b = exp2(m_c - M'), L = L*a + l_c*b, A = A*a + acc_c*b);
-//   * O = L > 0 ? A / L : 0 (IEEE division) times v_descale, rounded once to bf16.
+//   * O = L > 0 ? A / L : 0 (IEEE division) times v_descale, plus +0 (which
+//     turns a -0 into +0 and leaves every other value as it is), rounded once
+//     to bf16.
 //
-// All code is built with -ffp-contract=off: the compiler fuses no multiply-add,
-// so apart from the one explicit fused multiply-add in the exponent, each
-// product and sum above is a separately rounded fp32 operation in every kernel.
+// All code is built with -ffp-contract=off: the compiler fuses no multiply-add.
+// The op sequence holds exactly three fused multiply-adds, written explicitly
+// and run identically by every kernel: p = exp2(fma(s, c, -m')) in the block
+// update, and L = fma(L, a, l_c * b) and A = fma(A, a, acc_c * b) in the chunk
+// fold.  Every other product and sum above is a separately rounded fp32
+// operation.
+//
+// "Untouched" holds up to the sign of zero: a fully masked block leaves m and
+// l bit for bit, and acc too except that an accumulator element that is -0
+// (acc * alpha rounds to -0 when alpha underflows) can become +0 by adding the
+// block's +0 products.  One tiling computes such a block for a row and another
+// skips it, so the finalize step maps -0 to +0; a zero's sign then never
+// reaches O, and rows agree bit for bit across tilings and schedules.
 #pragma once
 
 #include "common.hpp"
@@ -334,7 +346,8 @@ __device__ __forceinline__ float merge_elem(float A, float acc, bool keep, float
 
 __device__ __forceinline__ float finalize_elem(float A, float L, float v_descale) {
   const float o = (L > 0.0f) ? (A / L) : 0.0f;
-  return o * v_descale;
+  // x + 0 is x for every x except -0, which becomes +0 (round to nearest even).
+  return o * v_descale + 0.0f;
 }
 // Natural-log sum of exp(scale * q.k): M is kept in log2 units.
 __device__ __forceinline__ float finalize_lse(float M, float L) {

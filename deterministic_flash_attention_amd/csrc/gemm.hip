@@ -333,26 +333,36 @@ __global__ __launch_bounds__(WM * WN * 64, WM * WN >= 8 ? 1 : 2) void gemm_kerne
 }
 
 // Split schedule, second pass: C = bf16(((p_0 + p_1) + p_2) + ...), the same
-// left fold the monolithic kernel runs in registers.  One thread per 4
-// consecutive columns.
-__global__ __launch_bounds__(256) void gemm_combine_kernel(const GemmParams p) {
-  const int64_t quads = p.m * (p.n / 4);
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= quads) return;
-  const int64_t row = idx / (p.n / 4), col = 4 * (idx % (p.n / 4));
+// left fold the monolithic kernel runs in registers.  A workgroup owns 1024
+// consecutive columns of one row (one thread per 4 columns), so its
+// descriptors are uniform: the partial rows are read and the C row stored
+// through descriptors whose num_records ends at column n, and threads past the
+// row's last column quad park their offsets beyond it.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineCols = 4 * kCombineThreads;
+
+__global__ __launch_bounds__(kCombineThreads) void gemm_combine_kernel(const GemmParams p) {
+  const int64_t col_blocks = (p.n + kCombineCols - 1) / kCombineCols;
+  const int64_t row = (int64_t)blockIdx.x / col_blocks;
+  const int64_t col = (int64_t)(blockIdx.x % col_blocks) * kCombineCols + 4 * threadIdx.x;
   const int64_t plane = p.m * p.n;
-  const float* src = p.part + row * p.n + col;
+  const uint32_t in_off = col < p.n ? (uint32_t)(col * 4) : kParkedOff;
   f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (p.nchunks > 0) t = *reinterpret_cast<const f32x4*>(src);
-  for (int c = 1; c < p.nchunks; ++c) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(src + c * plane);
+  for (int c = 0; c < p.nchunks; ++c) {
+    const rsrc_t rp = make_rsrc(p.part + c * plane + row * p.n, (uint32_t)(p.n * 4));
+    const f32x4 v = __builtin_bit_cast(f32x4, buf_load16(rp, in_off));
+    if (c == 0) {
+      t = v;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) t[e] = t[e] + v[e];
+      for (int e = 0; e < 4; ++e) t[e] = t[e] + v[e];
+    }
   }
   u32x2 o;
   o[0] = pack_bf16x2(t[0], t[1]);
   o[1] = pack_bf16x2(t[2], t[3]);
-  *reinterpret_cast<u32x2*>(static_cast<unsigned char*>(p.c) + (row * p.ldc + col) * 2) = o;
+  const rsrc_t rc = make_rsrc(static_cast<unsigned char*>(p.c) + row * p.ldc * 2, (uint32_t)(p.n * 2));
+  buf_store8(rc, col < p.n ? (uint32_t)(col * 2) : kParkedOff, o);
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES>
@@ -404,8 +414,8 @@ hipError_t launch_gemm(const GemmParams& p, int config, bool kn, bool split, hip
   }
   // Split combine; also the whole job when K = 0 (C = +0).
   if (p.m > 0 && p.n > 0 && (split || p.nchunks == 0)) {
-    const int64_t quads = p.m * (p.n / 4);
-    hipLaunchKernelGGL(gemm_combine_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+    const int64_t blocks = p.m * ((p.n + kCombineCols - 1) / kCombineCols);
+    hipLaunchKernelGGL(gemm_combine_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
                        stream, p);
     return hipGetLastError();
   }

@@ -28,15 +28,15 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
   constexpr int PER = D / 64;
   constexpr int kBatch = 8;  // accumulators in flight per wave
   const int lane = threadIdx.x & 63;
-  const int64_t rh = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  const int64_t rh = (int64_t)blockIdx.x * kMergeWaves + uniform((int)(threadIdx.x >> 6));
   const int64_t nrh = p.rows * p.hq;
-  if (rh >= nrh) return;
+  const bool valid = rh < nrh;  // wave-uniform; the last workgroup may hold idle waves
 
   float M = -INFINITY, L = 0.0f;
   float A[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) A[k] = 0.0f;
-  for (int c0 = 0; c0 < p.cmax; c0 += 64) {
+  for (int c0 = 0; valid && c0 < p.cmax; c0 += 64) {
     // Lane c holds the (m, l) of chunk c0 + c; chunks past cmax read as empty.
     float mc = -INFINITY, lc = 0.0f;
     if (c0 + lane < p.cmax) {
@@ -80,10 +80,20 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
       }
     }
   }
-  uint16_t* o = static_cast<uint16_t*>(p.o) + rh * D;
+  // Bounded epilogue: the wave's O row (and lse cell) through descriptors that
+  // end at its last valid byte; an idle wave's descriptors hold zero records,
+  // and lanes other than lane 0 park their lse store past the bound, so
+  // nothing outside the (row, head) cells is ever written.
+  const int64_t base = valid ? rh : 0;
+  const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + base * D * 2,
+                               valid ? (uint32_t)(D * 2) : 0u);
 #pragma unroll
-  for (int k = 0; k < PER; ++k) o[lane + 64 * k] = bf16_bits(finalize_elem(A[k], L, p.v_descale));
-  if (p.lse != nullptr && lane == 0) p.lse[rh] = finalize_lse(M, L);
+  for (int k = 0; k < PER; ++k)
+    buf_store2(orr, (uint32_t)(lane + 64 * k) * 2u, bf16_bits(finalize_elem(A[k], L, p.v_descale)));
+  if (p.lse != nullptr) {
+    const rsrc_t lr = make_rsrc(p.lse + base, valid ? 4u : 0u);
+    buf_store4(lr, lane == 0 ? 0u : kParked, f32_bits(finalize_lse(M, L)));
+  }
 }
 
 }  // namespace

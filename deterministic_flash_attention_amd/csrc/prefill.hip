@@ -441,10 +441,11 @@ void prefill_kernel(const PrefillParams p) {
   const int lo = row_lo(pos(qrow)), hi = row_hi(pos(qrow));
   // Blocks [wblk_first, wblk_end) hold a key visible to some row of this wave;
   // the others are fully masked for all of its rows (a wave whose rows all lie
-  // past the sequence has none).  Such a block leaves m, l and acc exactly as
-  // they were (alpha = 1, p = 0, and acc, which starts at +0, is never -0, so
-  // adding zero products changes no bit), so the wave skips its arithmetic
-  // while still taking part in the staging and the barriers.
+  // past the sequence has none).  Such a block leaves m and l exactly as they
+  // were (alpha = 1, p = 0) and acc up to the sign of a zero element (adding
+  // zero products can turn -0 into +0), which the finalize step erases, so the
+  // wave skips its arithmetic while still taking part in the staging and the
+  // barriers.
   const int wrow0 = r0 + 32 * ((int)uniform(wave) % C::kQGroups);
   const int wrow_last = min(wrow0 + 31, nrows - 1);
   const bool wactive = wrow0 < nrows;

@@ -141,18 +141,6 @@ def assert_bitwise(a: torch.Tensor, b: torch.Tensor, label: str) -> None:
     assert same, f"{label}: not bitwise identical"
 
 
-def sample_rows(seqlens, per_seq: int, seed: int) -> np.ndarray:
-    """Global row indices: per sequence the first, last and random rows."""
-    rng = np.random.default_rng(seed)
-    rows, start = [], 0
-    for n in seqlens:
-        if n > 0:
-            pick = {0, n - 1} | set(rng.integers(0, n, size=min(per_seq, n)).tolist())
-            rows.extend(start + r for r in sorted(pick))
-        start += n
-    return np.array(rows, dtype=np.int64)
-
-
 # ---------------------------------------------------------------- GEMM
 def gemm_views(inp: synth.GemmInputs, device="cuda"):
     """Device views of the (possibly row-padded) operands: A [M, K] with lda =

@@ -11,7 +11,7 @@ import torch
 
 import synth
 from gpu_utils import (assert_bitwise, compare, dev, note, oracle_extend, run_decode,
-                       run_extend, run_prefill, sample_rows)
+                       run_extend, run_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -126,14 +126,17 @@ def test_extend_sentinel_outside_valid_rows():
     assert not torch.any(view == 7.0), "a valid row was not written"
 
 
-def test_full_mixed_workload_sampled():
+def test_full_mixed_workload():
     """The benchmark's mixed batch at full size: prefill, extend and decode
-    sequences in one launch; sampled rows against the oracle."""
+    sequences in one launch, monolithic and split + merge (bit for bit the
+    same), against the oracle on every element."""
     cfg = synth.MIXED_EXTEND
     inp = synth.extend_inputs(0, cfg["ctx_lens"], cfg["q_lens"], cfg["hq"], cfg["hkv"], cfg["d"],
                               spare_pages=cfg["spare_pages"])
     note("full mixed paged-extend workload")
     o = run_extend(inp, MONO)
-    rows = sample_rows(cfg["q_lens"], 24, 11)
-    ref, _ = oracle_extend(inp, rows=rows)
-    compare(o, ref, False, rows=rows, label="O full mixed extend (sampled)")
+    o_split = run_extend(inp, SPLIT)
+    assert_bitwise(o_split, o, "mixed workload split vs monolithic")
+    note("oracle on every row")
+    ref, _ = oracle_extend(inp)
+    compare(o, ref, False, label=f"O full mixed extend (all {ref.size} elements)")

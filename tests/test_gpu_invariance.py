@@ -239,3 +239,68 @@ def test_e4m3_widening_every_code(d):
         o = run_decode(dec, sched).cpu().reshape(nrows, 1, d)
         assert torch.isnan(o[nan]).all(), "NaN codes must widen to NaN"
         assert_bitwise(o[~nan], want[~nan], f"decode schedule {sched}")
+
+
+def _zero_sign_inputs():
+    """One sequence of 200 keys (D=64, one head) built so that row 100's
+    accumulator holds -0 in column 5 before a block that is fully masked for
+    it: its block-0 scores are O(10) (log2 units) and V[:, 5] = -1 there, so
+    acc[5] < 0; key 90 scores about 288 (log2 units), so at block 1 alpha =
+    exp2(m - m') underflows to 0, acc[5] * 0 = -0, and every product of block 1
+    in that column is -0 (p = 1 times V[90, 5] = -0, p = 0 times -1).  Keys from
+    128 on have V[:, 5] = +1, so a computed fully masked block 2 adds +0 products
+    and can turn that -0 into +0."""
+    n, d, r, ks, col = 200, 64, 100, 90, 5
+    inp = synth.prefill_inputs(71, [n], 1, 1, d, True)
+    q, k, v = inp.q.clone(), inp.k.clone(), inp.v.clone()
+    q[r, 0] = 0.0
+    q[r, 0, 0] = 40.0
+    k[ks, 0] = 0.0
+    k[ks, 0, 0] = 40.0
+    v[:128, 0, col] = -1.0
+    v[ks, 0, col] = -0.0
+    v[128:, 0, col] = 1.0
+    return q, k, v, n, d, r, ks, col, inp.scale
+
+
+def test_zero_sign_under_alpha_underflow():
+    """Fully masked blocks leave a row untouched (RL-Kernel page, section 2)
+    up to the sign of zero, which the finalize step canonicalises: the prefill
+    tiling (row 100's wave stops at block 1), the extend tiling with one cached
+    token less of queries (row 100's wave reaches block 2, fully masked for
+    it), split or monolithic, the paged extend and the decode of the same row
+    agree bit for bit, and the row equals V[90] with the -0 written as +0."""
+    import deterministic_flash_attention_amd as dfa
+    q, k, v, n, d, r, ks, col, scale = _zero_sign_inputs()
+    pre = synth.PrefillInputs(q, k, v, synth.cu_seqlens([n]), synth.cu_seqlens([n]), [n], [n],
+                              1, 1, d, scale, True)
+    o_pre = run_prefill(pre, MONO).cpu()
+    ext = synth.PrefillInputs(q[1:].contiguous(), k, v, synth.cu_seqlens([n - 1]),
+                              synth.cu_seqlens([n]), [n - 1], [n], 1, 1, d, scale, True)
+    want = v[ks, 0].clone()
+    want[col] = 0.0  # +0: the canonical zero
+    assert_bitwise(o_pre[r, 0], want, "prefill row 100 = V[90] with +0")
+    for sched in (MONO, SPLIT):
+        o_ext = run_prefill(ext, sched).cpu()
+        assert_bitwise(o_ext[r - 1], o_pre[r], f"extend (schedule {sched}) vs prefill row")
+        assert_bitwise(o_ext, o_pre[1:], f"every extend row (schedule {sched}) vs prefill")
+    # The same row as a decode step over a paged copy of keys 0..100, and
+    # as a row of a paged extend launch.
+    ps = 16
+    npg = (n + ps - 1) // ps
+    kc = torch.zeros(npg, ps, 1, d, dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kc.view(-1, 1, d)[:n] = k
+    vc.view(-1, 1, d)[:n] = v
+    table = torch.arange(npg, dtype=torch.int32).reshape(1, npg)
+    dec = synth.DecodeInputs(q[r:r + 1].contiguous(), kc, vc, table,
+                             torch.tensor([r + 1], dtype=torch.int32), 1, 1, d, ps, scale)
+    for sched in (SPLIT, MONO):
+        assert_bitwise(run_decode(dec, sched).cpu()[0], o_pre[r], f"decode (schedule {sched})")
+    pext = synth.ExtendInputs(q[1:].contiguous(), synth.cu_seqlens([n - 1]), None, k, v,
+                              synth.cu_seqlens([n]), kc, vc, table,
+                              torch.tensor([n], dtype=torch.int32), [n - 1], [n], 1, 1, d, ps,
+                              scale, True)
+    from gpu_utils import run_extend
+    for sched in (MONO, SPLIT):
+        assert_bitwise(run_extend(pext, sched).cpu(), o_pre[1:], f"paged extend (schedule {sched})")

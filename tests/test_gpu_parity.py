@@ -8,8 +8,8 @@ import torch
 
 import oracle
 import synth
-from gpu_utils import (compare, note, oracle_inputs_prefill, run_decode, run_prefill,
-                       sample_rows)
+from gpu_utils import (assert_bitwise, compare, dev, note, oracle_inputs_prefill, run_decode,
+                       run_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -139,44 +139,111 @@ def test_decode_zero_context():
     assert torch.all(o[0].float() == 0)
 
 
-# ------------------------------------------- full-size workloads, sampled rows
-def test_full_dense_prefill_sampled():
-    cfg = synth.DENSE_PREFILL
-    rows = sample_rows(cfg["seqlens"], 48, 1)
-    _prefill_case(cfg["seqlens"], None, cfg["hq"], cfg["hkv"], cfg["d"], False, "bf16", 0, MONO,
-                  rows=rows)
+# ------------------------------------- full-size workloads, every element
+# Each workload at its full size, in both schedules (split = the split kernel
+# plus attn_chunk_merge), against the oracle on every row, head and column;
+# max_abs and mean_abs are taken over all elements.  The schedules must also
+# agree bit for bit.
+def _full_prefill(cfg, causal, dtype):
+    inp = synth.prefill_inputs(0, cfg["seqlens"], cfg["hq"], cfg["hkv"], cfg["d"], causal,
+                               dtype=dtype)
+    note(f"full {cfg['name']} {dtype} causal={causal}: GPU monolithic and split")
+    o_mono, lse_mono = run_prefill(inp, MONO, return_lse=True)
+    o_split, lse_split = run_prefill(inp, SPLIT, return_lse=True)
+    assert_bitwise(o_split, o_mono, "O split vs monolithic")
+    assert_bitwise(lse_split, lse_mono, "lse split vs monolithic")
+    note("oracle on every row")
+    q, k, v = oracle_inputs_prefill(inp)
+    ref, ref_lse = oracle.attention(q, k, v, inp.cu_seqlens_q.numpy(), inp.cu_seqlens_k.numpy(),
+                                    cfg["hq"], cfg["hkv"], inp.scale, causal)
+    for name, o, lse in (("monolithic", o_mono, lse_mono), ("split", o_split, lse_split)):
+        compare(o, ref, dtype == "fp8", label=f"O {name} (all {ref.size} elements)")
+        lg = lse.cpu().double().numpy()
+        assert np.array_equal(np.isneginf(lg), np.isneginf(ref_lse))
+        fin = np.isfinite(ref_lse)
+        assert np.abs(lg[fin] - ref_lse[fin]).max() < 2e-3
 
 
-def test_full_causal_varlen_sampled():
-    cfg = synth.CAUSAL_VARLEN
-    rows = sample_rows(cfg["seqlens"], 24, 2)
-    _prefill_case(cfg["seqlens"], None, cfg["hq"], cfg["hkv"], cfg["d"], True, "bf16", 0, MONO,
-                  rows=rows)
+def test_full_dense_prefill():
+    _full_prefill(synth.DENSE_PREFILL, False, "bf16")
+
+
+def test_full_causal_varlen():
+    _full_prefill(synth.CAUSAL_VARLEN, True, "bf16")
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_full_fp8_wide_head_sampled(causal):
-    cfg = synth.FP8_WIDE
-    rows = sample_rows(cfg["seqlens"], 32, 3)
-    _prefill_case(cfg["seqlens"], None, cfg["hq"], cfg["hkv"], cfg["d"], causal, "fp8", 0, MONO,
-                  rows=rows)
+def test_full_fp8_wide_head(causal):
+    _full_prefill(dict(synth.FP8_WIDE, causal=causal), causal, "fp8")
 
 
-def test_full_paged_decode_sampled_sequences():
+def test_full_tiny_causal_gqa():
+    _full_prefill(synth.TINY_CAUSAL, True, "bf16")
+
+
+def test_full_paged_decode_every_sequence():
+    """All 64 sequences of the paged decode workload, split + merge and
+    monolithic, over the tokens-outer ("NHD") cache and the heads-outer ("HND")
+    cache the benchmark times, each against the oracle on every element;
+    dead slots and spare pages hold NaN."""
+    import deterministic_flash_attention_amd as dfa
     cfg = synth.PAGED_DECODE
     inp = synth.decode_inputs(0, cfg["batch"], cfg["hq"], cfg["hkv"], cfg["d"],
                               ctx_min=cfg["ctx_min"], ctx_max=cfg["ctx_max"],
                               spare_pages=cfg["spare_pages"])
-    note(f"full decode: sum ctx = {int(inp.context_lens.sum())}")
-    o = run_decode(inp, SPLIT)
-    pick = np.random.default_rng(4).choice(cfg["batch"], size=12, replace=False)
-    pt, ctx = inp.page_table.numpy(), inp.context_lens.numpy()
-    q = synth.to_f64(inp.q)
-    for b in pick:
-        j = torch.arange(int(ctx[b]))
-        pages = torch.from_numpy(pt[b]).long()[j // 16]
-        kb = inp.k_cache[pages, j % 16].double().numpy()
-        vb = inp.v_cache[pages, j % 16].double().numpy()
-        ref, _ = oracle.attention(q[b:b + 1], kb, vb, [0, 1], [0, int(ctx[b])], cfg["hq"],
-                                  cfg["hkv"], inp.scale, True)
-        compare(o[b:b + 1], ref, False, label=f"decode seq {b} ctx {ctx[b]}")
+    mc = int(inp.context_lens.max())
+    note(f"full decode: sum ctx = {int(inp.context_lens.sum())}, max ctx = {mc}")
+    outs = {}
+    for layout in ("NHD", "HND"):
+        kc, vc = inp.k_cache, inp.v_cache
+        if layout == "HND":
+            kc, vc = kc.permute(0, 2, 1, 3), vc.permute(0, 2, 1, 3)
+        kc, vc = dev(kc), dev(vc)
+        for sched in (SPLIT, MONO):
+            o, lse = dfa.decode(dev(inp.q), kc, vc, dev(inp.page_table), dev(inp.context_lens), mc,
+                                softmax_scale=inp.scale, schedule=sched, return_lse=True,
+                                kv_layout=layout)
+            torch.cuda.synchronize()
+            outs[(layout, sched)] = (o, lse)
+        del kc, vc
+    o_ref, lse_ref = outs[("NHD", SPLIT)]
+    for key, (o, lse) in outs.items():
+        assert_bitwise(o, o_ref, f"decode O {key} vs NHD split")
+        assert_bitwise(lse, lse_ref, f"decode lse {key} vs NHD split")
+    note("oracle on every sequence")
+    ref, ref_lse = oracle.paged_decode(synth.to_f64(inp.q), inp.k_cache.float().numpy(),
+                                       inp.v_cache.float().numpy(), inp.page_table.numpy(),
+                                       inp.context_lens.numpy(), cfg["hq"], cfg["hkv"], inp.scale,
+                                       inp.page_size)
+    for key, (o, lse) in outs.items():
+        compare(o, ref, False, label=f"decode O {key} (all {ref.size} elements)")
+        lg = lse.cpu().double().numpy()
+        assert np.abs(lg - ref_lse).max() < 2e-3
+
+
+def test_full_paged_decode_fp8():
+    """The e4m3 cache of the benchmark (heads-outer layout, split + merge and
+    monolithic) against the oracle on its dequantised values, every element."""
+    import deterministic_flash_attention_amd as dfa
+    cfg = synth.PAGED_DECODE
+    inp = synth.decode_inputs(0, cfg["batch"], cfg["hq"], cfg["hkv"], cfg["d"],
+                              ctx_min=cfg["ctx_min"], ctx_max=cfg["ctx_max"],
+                              spare_pages=cfg["spare_pages"], dtype="fp8")
+    mc = int(inp.context_lens.max())
+    note(f"full fp8 decode: sum ctx = {int(inp.context_lens.sum())}")
+    kc = dev(inp.k_cache.permute(0, 2, 1, 3))
+    vc = dev(inp.v_cache.permute(0, 2, 1, 3))
+    desc = (inp.q_scale, inp.k_scale, inp.v_scale)
+    o_split = dfa.decode(dev(inp.q), kc, vc, dev(inp.page_table), dev(inp.context_lens), mc,
+                         softmax_scale=inp.scale, schedule=SPLIT, descales=desc, kv_layout="HND")
+    o_mono = dfa.decode(dev(inp.q), kc, vc, dev(inp.page_table), dev(inp.context_lens), mc,
+                        softmax_scale=inp.scale, schedule=MONO, descales=desc, kv_layout="HND")
+    torch.cuda.synchronize()
+    assert_bitwise(o_split, o_mono, "fp8 decode split vs monolithic")
+    note("oracle on every sequence")
+    ref, _ = oracle.paged_decode(oracle.dequantize_e4m3(inp.q.numpy(), inp.q_scale),
+                                 oracle.dequantize_e4m3(inp.k_cache.numpy(), inp.k_scale),
+                                 oracle.dequantize_e4m3(inp.v_cache.numpy(), inp.v_scale),
+                                 inp.page_table.numpy(), inp.context_lens.numpy(), cfg["hq"],
+                                 cfg["hkv"], inp.scale, inp.page_size)
+    compare(o_split, ref, True, label=f"fp8 decode O (all {ref.size} elements)")

@@ -11,7 +11,7 @@ import torch
 import oracle
 import synth
 from gpu_utils import (assert_bitwise, compare, dev, note, oracle_inputs_prefill, run_decode,
-                       run_prefill, sample_rows)
+                       run_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -148,16 +148,18 @@ def test_window_paged_extend_equals_prefill():
     assert_bitwise(o_ext, o_pre[tail.to(o_pre.device)], "windowed extend rows vs prefill rows")
 
 
-def test_full_dense_sliding_window_sampled():
-    """The dense workload's shape with a causal 1024-key sliding window; sampled
-    rows against the oracle."""
+def test_full_dense_sliding_window():
+    """The dense workload's shape with a causal 1024-key sliding window,
+    monolithic and split + merge (bit for bit the same), against the oracle on
+    every element."""
     cfg = synth.DENSE_PREFILL
     inp = synth.prefill_inputs(0, cfg["seqlens"], cfg["hq"], cfg["hkv"], cfg["d"], True)
     note("full dense causal sliding window 1024")
     o = _prefill(inp, MONO, (1024, -1))
-    rows = sample_rows(cfg["seqlens"], 40, 13)
+    o_split = _prefill(inp, SPLIT, (1024, -1))
+    assert_bitwise(o_split, o, "sliding window split vs monolithic")
+    note("oracle on every row")
     q, k, v = oracle_inputs_prefill(inp)
     ref, _ = oracle.attention(q, k, v, inp.cu_seqlens_q.numpy(), inp.cu_seqlens_k.numpy(),
-                              cfg["hq"], cfg["hkv"], inp.scale, True, rows=rows,
-                              window=(1024, -1))
-    compare(o, ref, False, rows=rows, label="O dense sliding window (sampled)")
+                              cfg["hq"], cfg["hkv"], inp.scale, True, window=(1024, -1))
+    compare(o, ref, False, label=f"O dense sliding window (all {ref.size} elements)")
