@@ -26,7 +26,8 @@ __all__ = [
     "DetAttnError", "BF16", "FP8_E4M3", "MONOLITHIC", "SPLIT", "BLOCK_KEYS", "CHUNK_KEYS",
     "PAGE_SIZE", "library_path", "load_library", "attn_status_str", "attn_num_chunks",
     "attn_partials_bytes", "attn_prefill_fwd", "attn_decode_split_fwd", "attn_paged_extend_fwd",
-    "attn_chunk_merge", "prefill", "decode", "paged_extend", "WEIGHT_NK", "WEIGHT_KN",
+    "attn_chunk_merge", "attn_decode_fwd_noalloc", "DECODE_SCRATCH_BYTES", "prefill", "decode",
+    "paged_extend", "WEIGHT_NK", "WEIGHT_KN",
     "GEMM_BLOCK_K", "GEMM_CHUNK_K", "det_gemm_num_chunks", "det_gemm_workspace_bytes",
     "det_gemm_num_configs", "det_gemm_config_tile", "det_gemm_fwd", "gemm",
 ]
@@ -36,6 +37,7 @@ MONOLITHIC, SPLIT = 0, 1
 BLOCK_KEYS, CHUNK_KEYS, PAGE_SIZE = 64, 512, 16
 WEIGHT_NK, WEIGHT_KN = 0, 1
 GEMM_BLOCK_K, GEMM_CHUNK_K = 64, 1024
+DECODE_SCRATCH_BYTES = 128 << 20  # static partials of attn_decode_fwd_noalloc, per GPU
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB: Optional[ctypes.CDLL] = None
@@ -85,6 +87,11 @@ def load_library() -> ctypes.CDLL:
     lib.attn_paged_extend_fwd.restype = ctypes.c_int
     lib.attn_chunk_merge.argtypes = [c_p, c_sz, c_i64, c_i32, c_i32, c_i32, c_f32, c_p, c_p, c_p]
     lib.attn_chunk_merge.restype = ctypes.c_int
+    lib.attn_decode_fwd_noalloc.argtypes = [c_i32, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_i64,
+                                            c_p, c_i32, c_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                            c_i32, c_i32, c_f32, c_f32, c_f32, c_f32, c_p, c_p,
+                                            c_p]
+    lib.attn_decode_fwd_noalloc.restype = ctypes.c_int
     lib.det_gemm_num_chunks.argtypes = [c_i64]
     lib.det_gemm_num_chunks.restype = c_i32
     lib.det_gemm_workspace_bytes.argtypes = [c_i64, c_i64, c_i64]
@@ -220,6 +227,24 @@ def attn_chunk_merge(partials, rows: int, num_heads_q: int, max_chunks: int, hea
                               int(rows), int(num_heads_q), int(max_chunks), int(head_dim),
                               float(v_descale), _ptr(o), _ptr(lse), _stream(stream))
     _check("attn_chunk_merge", st)
+
+
+def attn_decode_fwd_noalloc(q, k_cache, v_cache, page_table, context_lens,
+                            max_context_len: int, softmax_scale: float, o, lse=None,
+                            descales=(1.0, 1.0, 1.0), window_left: int = -1, stream=None,
+                            kv_layout: str = "NHD") -> None:
+    """Mirror of the C ``attn_decode_fwd_noalloc``: split decode plus merge
+    with the partials in the library's static device scratch; ``o`` (and
+    ``lse``) are caller-provided, nothing is allocated."""
+    lib = load_library()
+    npages, psize, hkv, d, s_page, s_tok, s_head = _cache_geometry(k_cache, kv_layout)
+    st = lib.attn_decode_fwd_noalloc(
+        _dtype_code(q), _ptr(q), _ptr(k_cache), _ptr(v_cache), int(npages), int(s_page),
+        int(s_tok), int(s_head), _ptr(page_table), int(page_table.shape[1]), _ptr(context_lens),
+        int(max_context_len), int(window_left), int(q.shape[0]), int(psize), int(q.shape[1]),
+        int(hkv), int(d), float(softmax_scale), float(descales[0]), float(descales[1]),
+        float(descales[2]), _ptr(o), _ptr(lse), _stream(stream))
+    _check("attn_decode_fwd_noalloc", st)
 
 
 def _rows_ptr(t: Optional[torch.Tensor]) -> Tuple[Optional[int], int]:

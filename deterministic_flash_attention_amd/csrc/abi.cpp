@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "../../include/detattn.h"
 #include "../../include/detgemm.h"
@@ -68,6 +69,38 @@ int32_t gemm_auto_config(int64_t m, int64_t n, int64_t split_factor) {
     }
   }
   return best;
+}
+
+// Device scratch of the allocation-free decode entry point: the split
+// schedule's chunk partials of one call live here instead of in a caller
+// workspace.  Every GPU the library runs on holds its own copy for the life
+// of the process.  In host code `scratch` is only a host-side stand-in: its
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is passed to kernels.
+constexpr size_t kScratchBytes = DA_DECODE_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the current device (looked up on the first call
+// made with that device current).
+hipError_t scratch_on_current_device(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -358,6 +391,60 @@ da_status attn_chunk_merge(const float* partials, size_t partials_bytes, int64_t
   p.cmax = max_chunks;
   p.v_descale = v_descale;
   const hipError_t e = detattn::launch_merge(p, head_dim, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DA_OK : DA_ELAUNCH;
+}
+
+da_status attn_decode_fwd_noalloc(int32_t dtype, const void* q, const void* k_cache,
+                                  const void* v_cache, int64_t num_pages, int64_t page_stride,
+                                  int64_t token_stride, int64_t head_stride,
+                                  const int32_t* page_table, int32_t max_pages_per_seq,
+                                  const int32_t* context_lens, int32_t max_context_len,
+                                  int32_t window_left, int32_t batch, int32_t page_size,
+                                  int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                  float softmax_scale, float q_descale, float k_descale,
+                                  float v_descale, void* o, float* lse, void* stream) {
+  detattn::DecodeParams p{};
+  int32_t cmax = 0;
+  const da_status st = decode_setup(dtype, q, k_cache, v_cache, num_pages, page_stride,
+                                    token_stride, head_stride, page_table, max_pages_per_seq,
+                                    context_lens, max_context_len, window_left, batch, page_size,
+                                    num_heads_q, num_heads_kv, head_dim, softmax_scale, q_descale,
+                                    k_descale, v_descale, true, &p, &cmax);
+  if (st != DA_OK) return st;
+  if (!o || !aligned(o, 16) || (lse && !aligned(lse, 4))) return DA_EINVAL;
+  if (partials_bytes_or_max(batch, num_heads_q, cmax, head_dim) > kScratchBytes)
+    return DA_EWORKSPACE;
+  if (batch == 0) return DA_OK;
+  if (stream != nullptr) {
+    // The scratch address belongs to the current device; so must the stream.
+    int cur = -1;
+    hipDevice_t sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess ||
+        hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+      return DA_ELAUNCH;
+    if (sdev != cur) return DA_EINVAL;
+  }
+  float* part = nullptr;
+  if (scratch_on_current_device(&part) != hipSuccess) return DA_ELAUNCH;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (cmax > 0) {
+    // Split: every chunk slot c < cmax of every (row, head) is written (empty
+    // chunks as m = -inf, l = 0), so nothing left by an earlier call is read.
+    p.part_acc = part;
+    p.part_ml = part + (size_t)cmax * batch * num_heads_q * head_dim;
+    hipError_t e = detattn::launch_decode(p, head_dim, dtype == DA_FP8_E4M3, true, hs);
+    if (e != hipSuccess) return DA_ELAUNCH;
+  }
+  detattn::MergeParams mp{};
+  mp.part_acc = part;
+  mp.part_ml = part + (size_t)cmax * batch * num_heads_q * head_dim;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rows = batch;
+  mp.hq = num_heads_q;
+  mp.cmax = cmax;
+  mp.v_descale = v_descale;
+  const hipError_t e = detattn::launch_merge(mp, head_dim, hs);
   return e == hipSuccess ? DA_OK : DA_ELAUNCH;
 }
 

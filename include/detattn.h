@@ -191,6 +191,40 @@ da_status attn_chunk_merge(const float* partials, size_t partials_bytes, int64_t
                            int32_t num_heads_q, int32_t max_chunks, int32_t head_dim,
                            float v_descale, void* o, float* lse, void* stream);
 
+/*
+ * Allocation-free paged decode, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the split schedule of attn_decode_split_fwd followed by
+ * attn_chunk_merge in one call, with the chunk partials kept in a static
+ * device array of the library (DA_DECODE_SCRATCH_BYTES per GPU, held by every
+ * GPU the library runs on until the process ends) instead of a caller
+ * workspace.  Arguments are those of attn_decode_split_fwd without schedule
+ * and partials; o [batch, Hq, D] bf16 and lse [batch, Hq] fp32 (may be NULL)
+ * are caller-owned.  The result is bit-identical to split + merge (and to the
+ * monolithic schedule).
+ *   - Size limit: attn_partials_bytes(batch, Hq, attn_num_chunks(max_context_len),
+ *     head_dim) must not exceed DA_DECODE_SCRATCH_BYTES, else DA_EWORKSPACE
+ *     (checked on the host, nothing launched).
+ *   - Calls no allocating routine (no hipMalloc, hipFree or memset).  The
+ *     first call with a device current looks up that device's scratch
+ *     address (hipGetSymbolAddress) and keeps it; `stream` must belong to the
+ *     current device (DA_EINVAL otherwise).
+ *   - Every call on one GPU shares that GPU's scratch: calls that overlap on
+ *     one GPU (different streams, or host threads without ordering) race and
+ *     must be serialised by the caller.  Each call writes every partial it
+ *     reads, so nothing left by an earlier call is ever read.
+ */
+#define DA_DECODE_SCRATCH_BYTES ((size_t)128 << 20)
+da_status attn_decode_fwd_noalloc(int32_t dtype, const void* q, const void* k_cache,
+                                  const void* v_cache, int64_t num_pages, int64_t page_stride,
+                                  int64_t token_stride, int64_t head_stride,
+                                  const int32_t* page_table, int32_t max_pages_per_seq,
+                                  const int32_t* context_lens, int32_t max_context_len,
+                                  int32_t window_left, int32_t batch, int32_t page_size,
+                                  int32_t num_heads_q, int32_t num_heads_kv, int32_t head_dim,
+                                  float softmax_scale, float q_descale, float k_descale,
+                                  float v_descale, void* o, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,7 +34,8 @@ def test_header_declares_entry_points():
     names = declared_functions()
     assert names == sorted(["attn_status_str", "attn_num_chunks", "attn_partials_bytes",
                             "attn_prefill_fwd", "attn_decode_split_fwd",
-                            "attn_paged_extend_fwd", "attn_chunk_merge"])
+                            "attn_paged_extend_fwd", "attn_chunk_merge",
+                            "attn_decode_fwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -119,6 +120,40 @@ def _decode_args(**over):
 ])
 def test_decode_validation(lib, over, status):
     assert lib.attn_decode_split_fwd(*_decode_args(**over)) == status
+
+
+def _noalloc_args(**over):
+    a = dict(dtype=0, q=FAKE, kc=FAKE, vc=FAKE, num_pages=100, page_stride=16 * 8 * 128,
+             token_stride=8 * 128, head_stride=128, table=FAKE, max_pages=64, ctx=FAKE,
+             max_ctx=1024, wl=-1, batch=4, page_size=16, hq=32, hkv=8, d=128, scale=0.088,
+             qd=1.0, kd=1.0, vd=1.0, o=FAKE, lse=None, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(page_size=32), DA_EUNSUPPORTED),
+    (dict(max_ctx=64 * 16 + 1), DA_EINVAL),
+    (dict(o=None), DA_EINVAL),
+    (dict(o=FAKE + 2), DA_EINVAL),
+    (dict(d=96), DA_EUNSUPPORTED),
+    (dict(vd=2.0), DA_EINVAL),
+    # partials of 64 rows x 32 heads x 256 chunks x 130 x 4 B exceed the static scratch
+    (dict(batch=64, max_pages=8192, max_ctx=8192 * 16), DA_EWORKSPACE),
+])
+def test_decode_noalloc_validation(lib, over, status):
+    """The allocation-free decode rejects before any HIP call, so these run on
+    the CPU; an oversized request is DA_EWORKSPACE."""
+    assert lib.attn_decode_fwd_noalloc(*_noalloc_args(**over)) == status
+
+
+def test_decode_noalloc_limit_matches_header(lib):
+    import deterministic_flash_attention_amd as dfa
+    text = open(HEADER).read()
+    assert re.search(r"#define DA_DECODE_SCRATCH_BYTES \(\(size_t\)128 << 20\)", text)
+    assert dfa.DECODE_SCRATCH_BYTES == 128 << 20
+    # the full paged decode workload (64 sequences, contexts up to 32768) fits
+    assert lib.attn_partials_bytes(64, 32, 64, 128) <= dfa.DECODE_SCRATCH_BYTES
 
 
 def _extend_args(**over):
