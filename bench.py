@@ -42,8 +42,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--pmc-pass", action="store_true",
-                    help="one launch of each kernel plus a 256 MiB copy, for counter runs")
+    ap.add_argument("--pmc-pass", nargs="?", const="traffic", choices=["traffic", "prefill"],
+                    help="one launch per kernel for counter runs: 'traffic' (default; a "
+                         "256 MiB copy, the dense prefill, decode, GEMM) or 'prefill'")
+    ap.add_argument("--pmc-summary", nargs="+", metavar=("KIND", "CSV"),
+                    help="summarise rocprofv3 counter CSVs of a --pmc-pass KIND run")
     return ap.parse_args()
 
 
@@ -126,23 +129,48 @@ def run_prefill_fn(inp, t, schedule, window=(-1, -1)):
     return fn, o
 
 
-def prefill_entry(name, cfg, causal, dtype, iters, warmup, peak, peak_note, window=(-1, -1)):
+# ---------------------------------------------------------------- secondary lines
+# Each secondary line is set up once (inputs resident in HBM) and exposes one or
+# more named callables; the lines are then timed in REPS interleaved repetitions
+# (repetition r of every line before repetition r + 1 of any), ITERS timed calls
+# each, and report the median of the repetition means and the minimum call.
+REPS, ITERS, WARMUP = 3, 20, 3
+
+
+class Line:
+    def __init__(self, fns, finish):
+        self.fns = fns          # name -> callable (one launch sequence per call)
+        self.finish = finish    # dict name -> stats -> entry dict
+        self.times = {k: [] for k in fns}
+
+
+def stats(rep_ms):
+    """rep_ms: list over repetitions of per-call ms lists."""
+    import statistics
+    means = [sum(r) / len(r) for r in rep_ms]
+    return {"ms_median": statistics.median(means), "ms_min": min(min(r) for r in rep_ms),
+            "ms_rep_means": [round(m, 5) for m in means]}
+
+
+def prefill_line(name, cfg, causal, dtype, peak, peak_note, window=(-1, -1)):
     import oracle
     inp, t = prefill_workload(cfg, causal, dtype)
     fn, _ = run_prefill_fn(inp, t, 0, window)
-    ms, _ = timed(fn, iters, warmup)
     flops = oracle.attention_flops(cfg["seqlens"], cfg["seqlens"], cfg["hq"], cfg["d"], causal,
                                    window=window)
-    avg = sum(ms) / len(ms)
-    tf = flops / (avg * 1e-3) / 1e12
-    return {
-        "workload": name, "causal": causal, "dtype": dtype, "seqlens": cfg["seqlens"],
-        "window": list(window),
-        "hq": cfg["hq"], "hkv": cfg["hkv"], "d": cfg["d"], "flop": flops,
-        "ms_mean": avg, "ms_min": min(ms), "value": tf, "unit": "TFLOP/s",
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
-                     "frac": tf / peak, "traffic": None, "peak_note": peak_note},
-    }
+
+    def finish(st):
+        s = st["run"]
+        tf = flops / (s["ms_median"] * 1e-3) / 1e12
+        return {
+            "workload": name, "causal": causal, "dtype": dtype, "seqlens": cfg["seqlens"],
+            "window": list(window), "hq": cfg["hq"], "hkv": cfg["hkv"], "d": cfg["d"],
+            "flop": flops, **s, "value": tf, "unit": "TFLOP/s",
+            "tflops_at_min": flops / (s["ms_min"] * 1e-3) / 1e12,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                         "frac": tf / peak, "traffic": None, "peak_note": peak_note},
+        }
+    return Line({"run": fn}, finish)
 
 
 def decode_bytes(inp) -> int:
@@ -157,7 +185,7 @@ def decode_bytes(inp) -> int:
     return kv + b * hq * d * es + b * hq * d * 2 + 4 * int(pages.sum()) + 4 * b
 
 
-def decode_entry(iters, warmup, dtype="bf16"):
+def decode_line(dtype="bf16"):
     """The paged decode workload (bf16, or an e4m3 cache with per-tensor scales),
     cache pages stored heads-outer ("HND": each kv head's 16 page rows contiguous,
     5% faster than tokens-outer "NHD", timed beside it; the same bits)."""
@@ -172,13 +200,13 @@ def decode_entry(iters, warmup, dtype="bf16"):
     q = inp.q.to(dev)
     kc = inp.k_cache.permute(0, 2, 1, 3).contiguous().to(dev)
     vc = inp.v_cache.permute(0, 2, 1, 3).contiguous().to(dev)
+    kc_nhd, vc_nhd = inp.k_cache.to(dev), inp.v_cache.to(dev)
     pt, cl = inp.page_table.to(dev), inp.context_lens.to(dev)
     b, hq, d = inp.q.shape
     mc = int(inp.context_lens.max())
     cmax = dfa.attn_num_chunks(mc)
     part = torch.empty(dfa.attn_partials_bytes(b, hq, cmax, d) // 4, dtype=torch.float32, device=dev)
     o = torch.empty(b, hq, d, dtype=torch.bfloat16, device=dev)
-
     desc = (inp.q_scale, inp.k_scale, inp.v_scale)
 
     def split():
@@ -188,82 +216,87 @@ def decode_entry(iters, warmup, dtype="bf16"):
     def merge():
         dfa.attn_chunk_merge(part, b, hq, cmax, d, o, v_descale=desc[2])
 
-    def both():
+    def step():
         split()
         merge()
-    ms_split, _ = timed(split, iters, warmup)
-    ms_merge, _ = timed(merge, iters, warmup)
-    ms_step, _ = timed(both, iters, warmup)
-    kc_nhd, vc_nhd = inp.k_cache.to(dev), inp.v_cache.to(dev)
 
-    def both_nhd():
+    def step_nhd():
         dfa.attn_decode_split_fwd(q, kc_nhd, vc_nhd, pt, cl, mc, inp.scale, dfa.SPLIT,
                                   partials=part, descales=desc, kv_layout="NHD")
         merge()
-    ms_step_nhd, _ = timed(both_nhd, iters, warmup)
-    del kc_nhd, vc_nhd
+
     nbytes = decode_bytes(inp)
-    a_split = sum(ms_split) / iters
-    a_step = sum(ms_step) / iters
-    gbs_step = nbytes / (a_step * 1e-3) / 1e9
-    gbs_split = nbytes / (a_split * 1e-3) / 1e9
     part_bytes = int((inp.context_lens.long() + 511).div(512, rounding_mode="floor").sum()) * hq * (d + 2) * 4
-    return {
-        "workload": "paged_decode" if dtype == "bf16" else "paged_decode_fp8", "dtype": dtype,
-        "batch": b, "hq": hq, "hkv": inp.hkv, "d": d, "kv_layout": "HND",
-        "step_frac_of_hbm_nhd": nbytes / (sum(ms_step_nhd) / iters * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "sum_context": int(inp.context_lens.sum()), "bytes": nbytes,
-        "ms_split": a_split, "ms_merge": sum(ms_merge) / iters, "ms_step": a_step,
-        "value": gbs_step, "unit": "GB/s",
-        "partials_bytes_written": part_bytes,
-        "roofline": {"bound": "hbm", "achieved": gbs_split, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": gbs_split / PEAK_HBM_GBS,
-                     "traffic": counted_traffic(f"decode_split_{dtype}"),
-                     "kernel": "decode split"},
-        "step_frac_of_hbm": gbs_step / PEAK_HBM_GBS,
-    }
+
+    def finish(st):
+        gbs = lambda ms: nbytes / (ms * 1e-3) / 1e9  # noqa: E731
+        a_split, a_step = st["split"]["ms_median"], st["step"]["ms_median"]
+        return {
+            "workload": "paged_decode" if dtype == "bf16" else "paged_decode_fp8", "dtype": dtype,
+            "batch": b, "hq": hq, "hkv": inp.hkv, "d": d, "kv_layout": "HND",
+            "sum_context": int(inp.context_lens.sum()), "bytes": nbytes,
+            "ms_split": a_split, "ms_merge": st["merge"]["ms_median"], "ms_step": a_step,
+            "ms_step_min": st["step"]["ms_min"], "ms_split_min": st["split"]["ms_min"],
+            "ms_step_rep_means": st["step"]["ms_rep_means"],
+            "value": gbs(a_step), "unit": "GB/s",
+            "partials_bytes_written": part_bytes,
+            "roofline": {"bound": "hbm", "achieved": gbs(a_split), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": gbs(a_split) / PEAK_HBM_GBS,
+                         "traffic": counted_traffic(f"decode_split_{dtype}"),
+                         "kernel": "decode split"},
+            "step_frac_of_hbm": gbs(a_step) / PEAK_HBM_GBS,
+            "step_frac_of_hbm_nhd": gbs(st["step_nhd"]["ms_median"]) / PEAK_HBM_GBS,
+        }
+    return Line({"split": split, "merge": merge, "step": step, "step_nhd": step_nhd}, finish)
 
 
-def extend_entry(iters, warmup):
-    """The mixed prefill / extend / decode batch over a paged cache, one
-    monolithic launch of attn_paged_extend_fwd per step."""
+def extend_setup():
     import torch
-    import deterministic_flash_attention_amd as dfa
-    import oracle
     import synth
     cfg = synth.MIXED_EXTEND
     inp = synth.extend_inputs(0, cfg["ctx_lens"], cfg["q_lens"], cfg["hq"], cfg["hkv"], cfg["d"],
                               spare_pages=cfg["spare_pages"], poison=False)
     dev = torch.device("cuda")
-    q, cq = inp.q.to(dev), inp.cu_seqlens_q.to(dev)
-    kc, vc = inp.k_cache.to(dev), inp.v_cache.to(dev)
-    pt, cl = inp.page_table.to(dev), inp.context_lens.to(dev)
-    o = torch.empty_like(q)
+    t = dict(q=inp.q.to(dev), cq=inp.cu_seqlens_q.to(dev), kc=inp.k_cache.to(dev),
+             vc=inp.v_cache.to(dev), pt=inp.page_table.to(dev), cl=inp.context_lens.to(dev))
+    return cfg, inp, t
+
+
+def extend_line():
+    """The mixed prefill / extend / decode batch over a paged cache, one
+    monolithic launch of attn_paged_extend_fwd per step."""
+    import torch
+    import deterministic_flash_attention_amd as dfa
+    import oracle
+    cfg, inp, t = extend_setup()
+    o = torch.empty_like(t["q"])
     mq, mc = max(inp.q_lens), max(inp.ctx_lens)
 
     def fn():
-        dfa.attn_paged_extend_fwd(q, cq, kc, vc, pt, cl, mq, mc, inp.scale, True, dfa.MONOLITHIC,
-                                  o=o)
-    ms, _ = timed(fn, iters, warmup)
+        dfa.attn_paged_extend_fwd(t["q"], t["cq"], t["kc"], t["vc"], t["pt"], t["cl"], mq, mc,
+                                  inp.scale, True, dfa.MONOLITHIC, o=o)
     flops = oracle.attention_flops(inp.q_lens, inp.ctx_lens, cfg["hq"], cfg["d"], True)
-    avg = sum(ms) / len(ms)
-    tf = flops / (avg * 1e-3) / 1e12
-    return {
-        "workload": "mixed_paged_extend", "causal": True, "dtype": "bf16",
-        "ctx_lens": inp.ctx_lens, "q_lens": inp.q_lens, "hq": cfg["hq"], "hkv": cfg["hkv"],
-        "d": cfg["d"], "flop": flops, "ms_mean": avg, "ms_min": min(ms), "value": tf,
-        "unit": "TFLOP/s",
-        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "prefill_kernel<128, bf16, paged, monolithic>"},
-    }
+
+    def finish(st):
+        s = st["run"]
+        tf = flops / (s["ms_median"] * 1e-3) / 1e12
+        return {
+            "workload": "mixed_paged_extend", "causal": True, "dtype": "bf16",
+            "ctx_lens": inp.ctx_lens, "q_lens": inp.q_lens, "hq": cfg["hq"], "hkv": cfg["hkv"],
+            "d": cfg["d"], "flop": flops, **s, "value": tf, "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                         "kernel": "prefill_kernel<128, bf16, paged, monolithic>"},
+        }
+    return Line({"run": fn}, finish)
 
 
-def gemm_entry(name, m, n, k, iters, warmup):
+def gemm_line(name, m, n, k):
     """C = A W^T for one layer shape: monolithic schedule for large M, split over
     the 1024-wide chunks plus the combine pass for decode-sized M.  Large M is
     priced against the bf16 MFMA peak (2 M N K FLOP), decode-sized M against
-    HBM (the weight, A and C bytes)."""
+    HBM (the weight, A and C bytes).  torch.matmul (hipBLASLt, not batch
+    invariant) is timed beside it as context."""
     import torch
     import deterministic_flash_attention_amd as dfa
     import synth
@@ -274,32 +307,73 @@ def gemm_entry(name, m, n, k, iters, warmup):
     sched = dfa.SPLIT if split else dfa.MONOLITHIC
     ws = torch.empty(max(dfa.det_gemm_workspace_bytes(m, n, k) // 4, 4), dtype=torch.float32,
                      device="cuda")
+    wt = w.t()
 
     def fn():
         dfa.det_gemm_fwd(a, w, c, dfa.WEIGHT_NK, sched, -1, ws)
-    ms, _ = timed(fn, iters, warmup)
-    wt = w.t()
-    ms_ref, _ = timed(lambda: torch.matmul(a, wt), iters, warmup)
-    avg = sum(ms) / len(ms)
+
+    def ref():
+        torch.matmul(a, wt)
     flops = 2 * m * n * k
-    tf = flops / (avg * 1e-3) / 1e12
     nbytes = 2 * (m * k + n * k + m * n)
-    gbs = nbytes / (avg * 1e-3) / 1e9
-    if split:
-        roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "traffic": counted_traffic(f"gemm_{name}"),
-                "kernel": "gemm split + combine (one step)"}
-    else:
-        roof = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": tf / PEAK_BF16_TFLOPS, "traffic": counted_traffic(f"gemm_{name}"),
-                "kernel": "gemm monolithic"}
-    return {
-        "workload": f"gemm_{name}", "m": m, "n": n, "k": k, "dtype": "bf16",
-        "schedule": "split" if split else "monolithic", "flop": flops, "bytes": nbytes,
-        "ms_mean": avg, "ms_min": min(ms), "value": tf, "unit": "TFLOP/s", "gb_s": gbs,
-        "roofline": roof,
-        "context_torch_matmul_ms_min": min(ms_ref),
-    }
+
+    def finish(st):
+        s = st["run"]
+        avg = s["ms_median"]
+        tf = flops / (avg * 1e-3) / 1e12
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        if split:
+            roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": gbs / PEAK_HBM_GBS, "traffic": counted_traffic(f"gemm_{name}"),
+                    "kernel": "gemm split + combine (one step)"}
+        else:
+            roof = {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tf / PEAK_BF16_TFLOPS, "traffic": counted_traffic(f"gemm_{name}"),
+                    "kernel": "gemm monolithic"}
+        return {
+            "workload": f"gemm_{name}", "m": m, "n": n, "k": k, "dtype": "bf16",
+            "schedule": "split" if split else "monolithic", "flop": flops, "bytes": nbytes,
+            **s, "value": tf, "unit": "TFLOP/s", "gb_s": gbs, "roofline": roof,
+            "context_torch_matmul_ms_min": st["torch_matmul"]["ms_min"],
+        }
+    return Line({"run": fn, "torch_matmul": ref}, finish)
+
+
+def secondary_lines():
+    import synth
+    mixed = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+    lines = [
+        prefill_line("causal_gqa_varlen", synth.CAUSAL_VARLEN, True, "bf16", PEAK_BF16_TFLOPS,
+                     "bf16 dense MFMA"),
+        decode_line("bf16"),
+        decode_line("fp8"),
+        extend_line(),
+        prefill_line("sliding_window_1024", synth.DENSE_PREFILL, True, "bf16", PEAK_BF16_TFLOPS,
+                     "bf16 dense MFMA", window=(1024, -1)),
+    ]
+    for causal in (False, True):
+        lines.append(prefill_line("fp8_wide_head", synth.FP8_WIDE, causal, "fp8", mixed,
+                                  "QK^T on fp8 MFMA, PV on bf16 MFMA: half the FLOPs at each peak"))
+    for name, m, n, k in synth.GEMM_SHAPES:
+        lines.append(gemm_line(name, m, n, k))
+    return lines
+
+
+def run_secondary():
+    lines = secondary_lines()
+    for rep in range(REPS):
+        for ln in lines:
+            for name, fn in ln.fns.items():
+                ms, _ = timed(fn, ITERS, WARMUP if rep == 0 else 1, min_warm_s=0.3 if rep == 0 else 0.05)
+                ln.times[name].append(ms)
+    out = []
+    for ln in lines:
+        e = ln.finish({k: stats(v) for k, v in ln.times.items()})
+        if e["workload"] == "fp8_wide_head":
+            e["frac_of_bf16_peak"] = e["value"] / PEAK_BF16_TFLOPS
+            e["frac_of_fp8_peak"] = e["value"] / PEAK_FP8_TFLOPS
+        out.append(e)
+    return out
 
 
 def cpu_baseline(target_s: float = 12.0):
@@ -337,32 +411,130 @@ def cpu_baseline(target_s: float = 12.0):
             "seconds": dt, "host_cpus": len(os.sched_getaffinity(0))}
 
 
-def pmc_pass():
-    """One launch of each kernel and a copy of known size (256 MiB read, 256 MiB
-    written) whose counters calibrate FETCH_SIZE / WRITE_SIZE."""
+def pmc_pass(kind: str):
+    """Launches for counter runs (rocprofv3 --pmc), one dispatch per kernel in a
+    fixed order printed to stdout.  "traffic": a copy of known size (256 MiB read,
+    256 MiB written) that calibrates FETCH_SIZE / WRITE_SIZE, then the dense
+    prefill, the bf16 and e4m3 decode split and merge, and the four GEMM shapes.
+    "prefill": the prefill workloads whose SQ counters the profiles quote
+    (dense, causal GQA varlen, fp8 D=192 dense and causal, the mixed paged batch,
+    the sliding window)."""
     import torch
     import deterministic_flash_attention_amd as dfa
     import synth
     dfa.load_library()
-    src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    inp, t = prefill_workload(synth.DENSE_PREFILL, False, "bf16")
-    fn, _ = run_prefill_fn(inp, t, dfa.MONOLITHIC)
-    fn()
-    decode_entry(1, 0)
-    decode_entry(1, 0, dtype="fp8")
-    for name, m, n, k in synth.GEMM_SHAPES:
-        inp_g = synth.gemm_inputs(0, m, n, k)
-        dfa.gemm(inp_g.a.cuda(), inp_g.w.cuda())
-    torch.cuda.synchronize()
-    print("pmc pass done")
+    order = []
+
+    def run(label, fn):
+        fn()
+        torch.cuda.synchronize()
+        order.append(label)
+    if kind == "traffic":
+        src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        run("copy_256MiB", lambda: dst.copy_(src))
+        inp, t = prefill_workload(synth.DENSE_PREFILL, False, "bf16")
+        run("prefill_dense_bf16", run_prefill_fn(inp, t, dfa.MONOLITHIC)[0])
+        del inp, t
+        for dt in ("bf16", "fp8"):
+            ln = decode_line(dt)
+            run(f"decode_split_{dt}", ln.fns["split"])
+            run(f"merge_d128_{dt}", ln.fns["merge"])
+            del ln
+        for name, m, n, k in synth.GEMM_SHAPES:
+            inp_g = synth.gemm_inputs(0, m, n, k)
+            a, w = inp_g.a.cuda(), inp_g.w.cuda()
+            run(f"gemm_{name}", lambda: dfa.gemm(a, w))
+    elif kind == "prefill":
+        mixed = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+        lines = [("prefill_dense_bf16", prefill_line("dense", synth.DENSE_PREFILL, False, "bf16",
+                                                     PEAK_BF16_TFLOPS, "")),
+                 ("prefill_causal_varlen_bf16", prefill_line("causal", synth.CAUSAL_VARLEN, True,
+                                                             "bf16", PEAK_BF16_TFLOPS, "")),
+                 ("prefill_fp8_d192_dense", prefill_line("fp8", synth.FP8_WIDE, False, "fp8",
+                                                         mixed, "")),
+                 ("prefill_fp8_d192_causal", prefill_line("fp8", synth.FP8_WIDE, True, "fp8",
+                                                          mixed, "")),
+                 ("mixed_paged_extend", extend_line()),
+                 ("sliding_window_1024", prefill_line("win", synth.DENSE_PREFILL, True, "bf16",
+                                                      PEAK_BF16_TFLOPS, "", window=(1024, -1)))]
+        for label, ln in lines:
+            run(label, ln.fns["run"])
+    else:
+        raise ValueError(kind)
+    print("pmc pass dispatch order: " + ", ".join(order))
+
+
+# Library dispatches of each counter pass, in launch order (see pmc_pass).
+PMC_LABELS = {
+    "traffic": ["prefill_dense_bf16", "decode_split_bf16", "merge_d128_bf16", "decode_split_fp8",
+                "merge_d128_fp8", "gemm_gate_up", "gemm_down", "gemm_qkv_decode",
+                "gemm_qkv_decode_combine", "gemm_gate_up_decode", "gemm_gate_up_decode_combine"],
+    "prefill": ["prefill_dense_bf16", "prefill_causal_varlen_bf16", "prefill_fp8_d192_dense",
+                "prefill_fp8_d192_causal", "mixed_paged_extend", "sliding_window_1024"],
+}
+
+
+def pmc_summary(kind: str, csv_paths):
+    """Counter values per labelled dispatch from rocprofv3 counter_collection CSVs
+    of `bench.py --pmc-pass KIND`.  For "traffic" (one CSV with FETCH_SIZE, one
+    with WRITE_SIZE) it also writes profiles/hbm_traffic.json: KiB per dispatch
+    scaled by what the same counter reads for the 256 MiB copy."""
+    import csv
+    per = {}
+    for path in csv_paths:
+        disp = {}
+        for r in csv.DictReader(open(path)):
+            d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "grid": r["Grid_Size"],
+                                                       "vgpr": r["VGPR_Count"], "lds": r["LDS_Block_Size"],
+                                                       "c": {}})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        ids = sorted(disp)
+        lib = [i for i in ids if "detattn::" in disp[i]["name"]]
+        labels = PMC_LABELS[kind]
+        assert len(lib) == len(labels), f"{path}: {len(lib)} library dispatches, expected {len(labels)}"
+        for i, lab in zip(lib, labels):
+            e = per.setdefault(lab, {"kernel": disp[i]["name"].split("(")[0].replace("void ", ""),
+                                     "grid": disp[i]["grid"], "vgpr": disp[i]["vgpr"],
+                                     "lds": disp[i]["lds"], "counters": {}})
+            e["counters"].update(disp[i]["c"])
+        copies = [i for i in ids if "copyBuffer" in disp[i]["name"] and int(disp[i]["grid"]) == 131072]
+        if copies:
+            per.setdefault("copy_256MiB", {"counters": {}})["counters"].update(disp[copies[0]]["c"])
+    if kind == "traffic":
+        cf = per["copy_256MiB"]["counters"]["FETCH_SIZE"]
+        cw = per["copy_256MiB"]["counters"]["WRITE_SIZE"]
+        out = {"source_hash": _source_hash(), "fetch_scale": 256 * 1024 / cf,
+               "write_scale": 256 * 1024 / cw, "copy_fetch_kib": cf, "copy_write_kib": cw,
+               "kernels": {}}
+        for lab in PMC_LABELS["traffic"]:
+            if lab.endswith("_combine"):
+                continue
+            f = per[lab]["counters"]["FETCH_SIZE"]
+            w = per[lab]["counters"]["WRITE_SIZE"]
+            comb = per.get(lab + "_combine")
+            if comb:  # a decode-sized GEMM step is the split kernel plus its combine pass
+                f += comb["counters"]["FETCH_SIZE"]
+                w += comb["counters"]["WRITE_SIZE"]
+            out["kernels"][lab] = {"fetch_kib": f, "write_kib": w,
+                                   "hbm_bytes": f * 1024 * out["fetch_scale"] + w * 1024 * out["write_scale"]}
+        out["note"] = ("HBM bytes per dispatch from two rocprofv3 --pmc runs (FETCH_SIZE, then "
+                       "WRITE_SIZE, KiB per dispatch) of `python3 bench.py --pmc-pass traffic`, each "
+                       "scaled by what the same counter reads for a 256 MiB device copy in the same "
+                       "run (bench.py --pmc-summary traffic). source_hash covers "
+                       "deterministic_flash_attention_amd/csrc/*; bench.py reports traffic only while "
+                       "it matches.")
+        json.dump(out, open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w"), indent=1)
+    print(json.dumps(per, indent=1))
 
 
 def main():
     args = parse()
     if args.pmc_pass:
-        pmc_pass()
+        pmc_pass(args.pmc_pass)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1:])
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
@@ -390,24 +562,7 @@ def main():
     k_avg = sum(ms_kernel) / len(ms_kernel)
     achieved = flops / (k_avg * 1e-3) / 1e12
 
-    secondary = []
-    if not args.no_secondary:
-        secondary.append(prefill_entry("causal_gqa_varlen", synth.CAUSAL_VARLEN, True, "bf16",
-                                       20, 3, PEAK_BF16_TFLOPS, "bf16 dense MFMA"))
-        secondary.append(decode_entry(20, 3))
-        secondary.append(decode_entry(20, 3, dtype="fp8"))
-        secondary.append(extend_entry(20, 3))
-        secondary.append(prefill_entry("sliding_window_1024", synth.DENSE_PREFILL, True, "bf16",
-                                       20, 3, PEAK_BF16_TFLOPS, "bf16 dense MFMA",
-                                       window=(1024, -1)))
-        mixed = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
-        for causal in (False, True):
-            e = prefill_entry("fp8_wide_head", synth.FP8_WIDE, causal, "fp8", 20, 3, mixed,
-                              "QK^T on fp8 MFMA, PV on bf16 MFMA: half the FLOPs at each peak")
-            e["frac_of_bf16_peak"] = e["value"] / PEAK_BF16_TFLOPS
-            secondary.append(e)
-        for name, m, n, k in synth.GEMM_SHAPES:
-            secondary.append(gemm_entry(name, m, n, k, 20, 3))
+    secondary = [] if args.no_secondary else run_secondary()
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     props = torch.cuda.get_device_properties(0)
     line = {

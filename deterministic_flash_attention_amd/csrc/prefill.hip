@@ -25,6 +25,8 @@
 // valid row of the sequence (FlyDSL conv3d and aiter MQA-logits pages): padded
 // tail rows of a tile are dropped by the hardware range check, so they can
 // never land on the next sequence's rows.
+#include <type_traits>
+
 #include "contract.hpp"
 #include "kernels.hpp"
 
@@ -59,11 +61,23 @@ struct PrefillCfg {
       (PAGED && kDirect) ? (16 * G::kKRow + 1023) / 1024 * 1024 : 16 * G::kKRow;
   static constexpr int kKStage = 4 * kKPage;
   static constexpr int kVStage = G::kVStage;  // 16 V rows are whole 1 KB segments
+  // e4m3 wide heads from packed rows run the score/PV pair schedule: of the two
+  // waves that share a SIMD and a 32-row query group, the score wave (w < 4)
+  // computes the scores and the softmax of each block once and hands P and
+  // (alpha, m, l) to its PV wave (w + 4) through LDS, in two alternating P slots.
+  static constexpr bool kPairPC = FP8 && !PAGED && kDSplit == 2;
+  static constexpr int kPairTilesS = 2;                   // output tiles of a score wave
+  static constexpr int kPairTilesV = D / 32 - kPairTilesS;  // and of its PV wave
+  static constexpr int kPRow = kWave * 16;                // one u32x4 per lane
+  static constexpr int kPSlot = 5 * kPRow;                // P^T (4 rows) + (alpha, m, l)
   static constexpr int kKOff = kQBytes;
   static constexpr int kVOff = kKOff + 2 * kKStage;
-  static constexpr int kLds = kVOff + 2 * kVStage;
-  // Q tile, the two K stages and the two V stages are disjoint byte ranges.
-  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * kKStage, "LDS regions overlap");
+  static constexpr int kPOff = kVOff + 2 * kVStage;
+  static constexpr int kLds = kPOff + (kPairPC ? 2 * kQGroups * kPSlot : 0);
+  // Q tile, the two K stages, the two V stages and the P slots are disjoint
+  // byte ranges.
+  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * kKStage &&
+                kPOff >= kVOff + 2 * kVStage, "LDS regions overlap");
   static_assert(kDirect || kKPage == 16 * G::kKRow, "register staging writes row-major stages");
 };
 
@@ -312,6 +326,68 @@ struct PagedDirectStager {
   }
 };
 
+// Split schedule epilogue: the chunk partial of this wave's query row and
+// output tiles [dt0, dt0 + NT): (m, l) by one lane per row (lane half 0 of the
+// wave holding tile 0), acc by every lane; both through descriptors that end at
+// the sequence's last row.
+template <int D, int NT>
+__device__ __forceinline__ void store_partial(const PrefillParams& p, const f32x16 (&acc)[NT],
+                                              float m, float l, int dt0, int chunk,
+                                              int64_t q_start, int head, int nrows, int64_t rs,
+                                              int qrow, int h) {
+  const int64_t ml_head = ((int64_t)chunk * p.total_q + q_start) * p.hq + head;
+  const rsrc_t mlr = make_rsrc(p.part_ml + 2 * ml_head,
+                               extent_bytes(nrows, rs * 8, 8,
+                                            ((int64_t)(chunk + 1) * p.total_q * p.hq - ml_head) * 8));
+  buf_store8(mlr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(rs * 8),
+             u32x2{f32_bits(m), f32_bits(l)});
+  const int64_t acc_head = ml_head * D;
+  const rsrc_t ar = make_rsrc(p.part_acc + acc_head,
+                              extent_bytes(nrows, rs * D * 4, D * 4,
+                                           ((int64_t)(chunk + 1) * p.total_q * p.hq * D - acc_head) * 4));
+  const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(rs * D * 4);
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * (dt0 + j) + 8 * q4 + 4 * h;
+      buf_store16(ar, rowoff + (uint32_t)d * 4u,
+                  u32x4{f32_bits(acc[j][4 * q4 + 0]), f32_bits(acc[j][4 * q4 + 1]),
+                        f32_bits(acc[j][4 * q4 + 2]), f32_bits(acc[j][4 * q4 + 3])});
+    }
+}
+
+// Monolithic epilogue: O = A / L (times v_descale) for output tiles
+// [dt0, dt0 + NT) rounded once to bf16, and lse from the wave holding tile 0.
+template <int D, int NT>
+__device__ __forceinline__ void store_output(const PrefillParams& p, const f32x16 (&A)[NT],
+                                             float M, float L, int dt0, int64_t q_start, int head,
+                                             int nrows, int64_t rs, int qrow, int h) {
+  const int64_t o_head = (int64_t)q_start * p.hq + head;
+  const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + o_head * D * 2,
+                               extent_bytes(nrows, rs * D * 2, D * 2,
+                                            (p.total_q * p.hq - o_head) * D * 2));
+  const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(rs * D * 2);
+  const float vd = p.v_descale;
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * (dt0 + j) + 8 * q4 + 4 * h;
+      const uint32_t w0 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 0], L, vd),
+                                      finalize_elem(A[j][4 * q4 + 1], L, vd));
+      const uint32_t w1 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 2], L, vd),
+                                      finalize_elem(A[j][4 * q4 + 3], L, vd));
+      buf_store8(orr, rowoff + (uint32_t)d * 2u, u32x2{w0, w1});
+    }
+  if (p.lse != nullptr) {
+    const rsrc_t lr = make_rsrc(p.lse + o_head, extent_bytes(nrows, rs * 4, 4,
+                                                             (p.total_q * p.hq - o_head) * 4));
+    buf_store4(lr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(rs * 4),
+               f32_bits(finalize_lse(M, L)));
+  }
+}
+
 template <int D, bool FP8, int NW, int WPE, bool SPLIT, bool PAGED, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void prefill_kernel(const PrefillParams p) {
@@ -467,6 +543,209 @@ void prefill_kernel(const PrefillParams p) {
       buf_store8(mlr, off, u32x2{f32_bits(-INFINITY), 0u});
       return;
     }
+  }
+
+  if constexpr (C::kPairPC) {
+    // Score/PV pair schedule (e4m3 wide heads from packed rows).  Waves w and
+    // w + 4 share a SIMD and the 32 query rows of group qg = w % 4.  The score
+    // wave computes S_j = K_j Q^T and the softmax update of block j once, for
+    // both, and publishes P_j^T and (alpha_j, m_j, l_j) in P slot j % 2; every
+    // step j also applies block j - 1 to the output: the score wave to tiles
+    // [0, kPairTilesS), the PV wave, which reads P_{j-1} from the slot, to the
+    // other kPairTilesV.  The PV waves do all the staging: K_{j+1} straight
+    // into K stage (j+1) % 2 and V_j, widened to bf16, into V stage j % 2.
+    // One barrier per step.  Slot use per step j: QK_j reads K stage j % 2
+    // (filled in step j - 1); PV_{j-1} reads V stage (j-1) % 2 (filled in step
+    // j - 1) and P slot (j-1) % 2 (written in step j - 1); step j writes K
+    // stage (j+1) % 2 (last read in step j - 1), V stage j % 2 (last read in
+    // step j - 1) and P slot j % 2 (last read in step j - 1).  Every operand
+    // reaches the same MFMA and VALU operations as in the other schedules, so
+    // the bits are the same.
+    constexpr int NTS = C::kPairTilesS, NTV = C::kPairTilesV;
+    constexpr int kVChunks = kBlockKeys * G::kChunks16;  // 16-byte chunks of a V block
+    constexpr int kVPer = (kVChunks + 255) / 256;         // per PV-wave thread
+    const int wv = uniform(wave);
+    const bool score = wv < 4;
+    const int qgp = wv & 3;
+    const int dtp = score ? 0 : NTS;  // first output tile of this wave
+    unsigned char* const sP = smem + C::kPOff;
+    auto pslot = [&](int j) { return sP + ((j & 1) * C::kQGroups + qgp) * C::kPSlot; };
+    const float c = p.c_scale;
+    // The two roles run separate instantiations of the step loop, so each
+    // holds only its own accumulators and running totals in registers.
+    auto run_role = [&](auto role) {
+      constexpr bool S = decltype(role)::value;
+      constexpr int NTX = S ? NTS : NTV;
+      float m = -INFINITY, l = 0.0f, M = -INFINITY, L = 0.0f;
+      f32x16 acc[NTX], A[NTX];
+#pragma unroll
+      for (int t = 0; t < NTX; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[t][i] = A[t][i] = 0.0f;
+      auto softmax = [&](int blk, const f32x16 (&s)[2], float& alpha, u32x4 (&pb)[4]) {
+        const int b0 = kBlockKeys * blk;
+        if (b0 >= klo_full && b0 + kBlockKeys <= kfull) {
+          softmax_block<kNoMask>(s, h, c, 0, 0, m, l, alpha, pb);
+        } else if (b0 >= wlo_max) {
+          softmax_block<kMaskHi>(s, h, c, 0, hi - b0, m, l, alpha, pb);
+        } else {
+          softmax_block<kMaskLoHi>(s, h, c, lo - b0, hi - b0, m, l, alpha, pb);
+        }
+      };
+      // The fold of a finished chunk into the running total (the function
+      // every schedule runs); the accumulator restarts from +0.
+      auto fold = [&](float mc, float lc) {
+        float ca, cb;
+        bool keep;
+        merge_stats(M, L, mc, lc, ca, cb, keep);
+#pragma unroll
+        for (int t = 0; t < NTX; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            A[t][i] = merge_elem(A[t][i], acc[t][i], keep, ca, cb);
+            acc[t][i] = 0.0f;
+          }
+      };
+      if (blk_begin < blk_end) {
+        const int n = blk_end - blk_begin;
+        const int64_t q_head = (int64_t)q_start * p.hq + head;
+        const int64_t kv_head = (int64_t)k_start * p.hkv + g;
+        const uint32_t q_row_bytes = (uint32_t)(rs * G::kRowBytes);
+        const uint32_t kv_row_bytes = (uint32_t)(p.hkv * G::kRowBytes);
+        const unsigned char* qb = static_cast<const unsigned char*>(p.q) + q_head * G::kRowBytes;
+        const unsigned char* kb = static_cast<const unsigned char*>(p.k) + kv_head * G::kRowBytes;
+        const unsigned char* vb = static_cast<const unsigned char*>(p.v) + kv_head * G::kRowBytes;
+        const rsrc_t qr = make_rsrc(qb, extent_bytes(nrows, q_row_bytes, G::kRowBytes,
+                                                     (p.total_q * p.hq - q_head) * G::kRowBytes));
+        // Window-sized K/V descriptors over key rows [kstart, kend).
+        const uint32_t kv_ext =
+            extent_bytes(kend - kstart, kv_row_bytes, G::kRowBytes,
+                         (p.total_k * p.hkv - kv_head) * G::kRowBytes - (int64_t)kstart * kv_row_bytes);
+        const int64_t kv_win = (int64_t)kstart * kv_row_bytes;
+        const rsrc_t kr = make_rsrc(kb + kv_win, kv_ext);
+        const rsrc_t vr = make_rsrc(vb + kv_win, kv_ext);
+        // PV waves: direct K staging over their four waves, V through registers.
+        DirectStager<D, 4, true> kst;
+        const int vt = tid - 256;  // PV-wave thread index
+        u32x4 vreg[kVPer];
+        auto v_load = [&](int blk) {
+#pragma unroll
+          for (int u = 0; u < kVPer; ++u) {
+            const int x = vt + 256 * u;
+            if (kVPer * 256 == kVChunks || x < kVChunks) {
+              const int r = x / G::kChunks16, col = x % G::kChunks16;
+              vreg[u] = buf_load16(vr, (uint32_t)((int64_t)(blk * kBlockKeys - kstart + r) * kv_row_bytes) +
+                                           (uint32_t)col * 16u);
+            }
+          }
+        };
+        auto v_store = [&](unsigned char* vs) {
+#pragma unroll
+          for (int u = 0; u < kVPer; ++u) {
+            const int x = vt + 256 * u;
+            if (kVPer * 256 == kVChunks || x < kVChunks) {
+              const int r = x / G::kChunks16, col = x % G::kChunks16;
+              const u32x2 a = e4m3x4_to_bf16x4(vreg[u][0]), b2 = e4m3x4_to_bf16x4(vreg[u][1]);
+              const u32x2 c2 = e4m3x4_to_bf16x4(vreg[u][2]), d2 = e4m3x4_to_bf16x4(vreg[u][3]);
+              const uint32_t o = (uint32_t)(r * G::kVRow + col * 32);
+              lds_store16(vs, o, u32x4{a[0], a[1], b2[0], b2[1]});
+              lds_store16(vs, o + 16, u32x4{c2[0], c2[1], d2[0], d2[1]});
+            }
+          }
+        };
+        // Prologue: K_0 into K stage 0 and V_0 into registers (PV waves), the
+        // Q tile into LDS (every wave), then the score wave's Q^T operands.
+        if constexpr (!S) {
+          kst.init(wv - 4, lane, kr, vr, kv_row_bytes, kstart);
+          kst.issue_k(blk_begin, sK, wv - 4);
+          v_load(blk_begin);
+        }
+        for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
+          const int r = x / G::kChunks16, col = x % G::kChunks16;
+          lds_store16(sQ, (uint32_t)(r * G::kQRow + col * 16),
+                      buf_load16(qr, (uint32_t)(r0 + r) * q_row_bytes + (uint32_t)col * 16u));
+        }
+        wait_vm();
+        __syncthreads();
+        QOperands<D, true> qop;
+        if constexpr (S) qop.load(sQ + (32 * qgp + (lane & 31)) * G::kQRow, lane);
+        u32x4 pb_prev[4] = {};
+        float alpha_prev = 1.0f;
+        for (int j = 0; j <= n; ++j) {
+          const int blk = blk_begin + j;
+          // Block j - 1 is the last block of its chunk (or of the range).
+          const bool chunk_end = j > 0 && (blk % kBlocksPerChunk == 0 || j == n);
+          const bool live_prev = j > 0 && wave_live(blk - 1);
+          if constexpr (S) {
+            const float mc = m, lc = l;
+            if (chunk_end && j < n) {  // block j opens a new chunk from the empty state
+              m = -INFINITY;
+              l = 0.0f;
+            }
+            u32x4 pb[4];
+            float alpha = 1.0f;
+            if (j < n && wave_live(blk)) {
+              f32x16 sc[2];
+              qk_scores_qreg<D, true, C::kKPage>(sc, qop, sK + (j & 1) * C::kKStage, lane);
+              softmax(blk, sc, alpha, pb);
+              unsigned char* const ps = pslot(j);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) lds_store16(ps, (uint32_t)(k * C::kPRow + lane * 16), pb[k]);
+              lds_store16(ps, (uint32_t)(4 * C::kPRow + lane * 16),
+                          u32x4{f32_bits(alpha), f32_bits(m), f32_bits(l), 0u});
+            }
+            if (live_prev) {
+              rescale_acc<NTX>(acc, alpha_prev);
+              pv_mfma<D, NTX>(acc, 0, pb_prev, sV + ((j - 1) & 1) * C::kVStage, lane);
+            }
+            if constexpr (!SPLIT) {
+              if (chunk_end) fold(mc, lc);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) pb_prev[k] = pb[k];
+            alpha_prev = alpha;
+          } else {
+            if (j < n) v_store(sV + (j & 1) * C::kVStage);
+            if (j + 1 < n) {
+              kst.issue_k(blk + 1, sK + ((j + 1) & 1) * C::kKStage, wv - 4);
+              v_load(blk + 1);
+            }
+            if (live_prev) {
+              const unsigned char* const ps = pslot(j - 1);
+              u32x4 pb[4];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) pb[k] = lds_load16(ps, (uint32_t)(k * C::kPRow + lane * 16));
+              const u32x4 st = lds_load16(ps, (uint32_t)(4 * C::kPRow + lane * 16));
+              m = bits_f32(st[1]);
+              l = bits_f32(st[2]);
+              rescale_acc<NTX>(acc, bits_f32(st[0]));
+              pv_mfma<D, NTX>(acc, NTS, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
+            }
+            if constexpr (!SPLIT) {
+              if (chunk_end) {
+                fold(m, l);
+                m = -INFINITY;
+                l = 0.0f;
+              }
+            }
+          }
+          wait_vm();
+          __syncthreads();
+        }
+      }
+      // Epilogue: each wave stores its own output tiles.
+      if constexpr (SPLIT) {
+        store_partial<D, NTX>(p, acc, m, l, dtp, chunk, q_start, head, nrows, rs, qrow, h);
+      } else {
+        store_output<D, NTX>(p, A, M, L, dtp, q_start, head, nrows, rs, qrow, h);
+      }
+    };
+    if (score) {
+      run_role(std::true_type{});
+    } else {
+      run_role(std::false_type{});
+    }
+    return;
   }
 
   const float c = p.c_scale;
@@ -735,52 +1014,9 @@ void prefill_kernel(const PrefillParams p) {
   }
 
   if constexpr (SPLIT) {
-    const int64_t ml_head = ((int64_t)chunk * p.total_q + q_start) * p.hq + head;
-    const rsrc_t mlr = make_rsrc(p.part_ml + 2 * ml_head,
-                                 extent_bytes(nrows, rs * 8, 8,
-                                              ((int64_t)(chunk + 1) * p.total_q * p.hq - ml_head) * 8));
-    buf_store8(mlr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(rs * 8),
-               u32x2{f32_bits(m), f32_bits(l)});
-    const int64_t acc_head = ml_head * D;
-    const rsrc_t ar = make_rsrc(p.part_acc + acc_head,
-                                extent_bytes(nrows, rs * D * 4, D * 4,
-                                             ((int64_t)(chunk + 1) * p.total_q * p.hq * D - acc_head) * 4));
-    const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(rs * D * 4);
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * (dt0 + j) + 8 * q4 + 4 * h;
-        buf_store16(ar, rowoff + (uint32_t)d * 4u,
-                    u32x4{f32_bits(acc[j][4 * q4 + 0]),
-                          f32_bits(acc[j][4 * q4 + 1]),
-                          f32_bits(acc[j][4 * q4 + 2]),
-                          f32_bits(acc[j][4 * q4 + 3])});
-      }
+    store_partial<D, NT>(p, acc, m, l, dt0, chunk, q_start, head, nrows, rs, qrow, h);
   } else {
-    const int64_t o_head = (int64_t)q_start * p.hq + head;
-    const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + o_head * D * 2,
-                                 extent_bytes(nrows, rs * D * 2, D * 2,
-                                              (p.total_q * p.hq - o_head) * D * 2));
-    const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(rs * D * 2);
-    const float vd = p.v_descale;
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * (dt0 + j) + 8 * q4 + 4 * h;
-        const uint32_t w0 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 0], L, vd),
-                                        finalize_elem(A[j][4 * q4 + 1], L, vd));
-        const uint32_t w1 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 2], L, vd),
-                                        finalize_elem(A[j][4 * q4 + 3], L, vd));
-        buf_store8(orr, rowoff + (uint32_t)d * 2u, u32x2{w0, w1});
-      }
-    if (p.lse != nullptr) {
-      const rsrc_t lr = make_rsrc(p.lse + o_head, extent_bytes(nrows, rs * 4, 4,
-                                                               (p.total_q * p.hq - o_head) * 4));
-      buf_store4(lr, (h || dt0) ? kParked : (uint32_t)qrow * (uint32_t)(rs * 4),
-                 f32_bits(finalize_lse(M, L)));
-    }
+    store_output<D, NT>(p, A, M, L, dt0, q_start, head, nrows, rs, qrow, h);
   }
 }
 
