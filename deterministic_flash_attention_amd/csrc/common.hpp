@@ -49,6 +49,23 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, unsigned char* lds_seg,
       r, (__attribute__((address_space(3))) void*)lds_seg, 16, off, 0, 0, 0);
 }
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier that completes this wave's LDS operations (so its LDS
+// writes are visible to every wave after it) but not its vector-memory loads:
+// __syncthreads() also waits for every outstanding load (vmcnt(0)), which
+// would drain loads meant to stay in flight across the barrier.  Loads whose
+// data the next step reads must be waited for explicitly (wait_vm_n) before
+// it.  The memory clobber keeps the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (they complete in issue order for this count, so the oldest are done).
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);

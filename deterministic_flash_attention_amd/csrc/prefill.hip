@@ -69,15 +69,24 @@ struct PrefillCfg {
   static constexpr int kPairTilesS = 2;                   // output tiles of a score wave
   static constexpr int kPairTilesV = D / 32 - kPairTilesS;  // and of its PV wave
   static constexpr int kPRow = kWave * 16;                // one u32x4 per lane
-  static constexpr int kPSlot = 5 * kPRow;                // P^T (4 rows) + (alpha, m, l)
+  static constexpr int kPSlot = 4 * kPRow + 32 * 16;      // P^T + (alpha, m, l) per query column
   static constexpr int kKOff = kQBytes;
   static constexpr int kVOff = kKOff + 2 * kKStage;
-  static constexpr int kPOff = kVOff + 2 * kVStage;
-  static constexpr int kLds = kPOff + (kPairPC ? 2 * kQGroups * kPSlot : 0);
-  // Q tile, the two K stages, the two V stages and the P slots are disjoint
-  // byte ranges.
-  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * kKStage &&
-                kPOff >= kVOff + 2 * kVStage, "LDS regions overlap");
+  static constexpr int kEnd = kVOff + 2 * kVStage;
+  // Pair schedule layout: three K stages (K reaches LDS two blocks ahead), two
+  // V stages and the P slots; no Q tile (the score waves read their Q^T operands
+  // straight into registers).
+  static constexpr int kPcKStages = 3;
+  static constexpr int kPcKOff = 0;
+  static constexpr int kPcVOff = kPcKOff + kPcKStages * kKStage;
+  static constexpr int kPcPOff = kPcVOff + 2 * kVStage;
+  static constexpr int kPcEnd = kPcPOff + 2 * kQGroups * kPSlot;
+  static constexpr int kLds = kPairPC ? kPcEnd : kEnd;
+  // Q tile, the K stages, the V stages and the P slots are disjoint byte ranges.
+  static_assert(kKOff >= kQBytes && kVOff >= kKOff + 2 * kKStage && kEnd >= kVOff + 2 * kVStage,
+                "LDS regions overlap");
+  static_assert(kPcVOff >= kPcKOff + kPcKStages * kKStage && kPcPOff >= kPcVOff + 2 * kVStage,
+                "LDS regions overlap");
   static_assert(kDirect || kKPage == 16 * G::kKRow, "register staging writes row-major stages");
 };
 
@@ -549,27 +558,36 @@ void prefill_kernel(const PrefillParams p) {
     // Score/PV pair schedule (e4m3 wide heads from packed rows).  Waves w and
     // w + 4 share a SIMD and the 32 query rows of group qg = w % 4.  The score
     // wave computes S_j = K_j Q^T and the softmax update of block j once, for
-    // both, and publishes P_j^T and (alpha_j, m_j, l_j) in P slot j % 2; every
-    // step j also applies block j - 1 to the output: the score wave to tiles
-    // [0, kPairTilesS), the PV wave, which reads P_{j-1} from the slot, to the
-    // other kPairTilesV.  The PV waves do all the staging: K_{j+1} straight
-    // into K stage (j+1) % 2 and V_j, widened to bf16, into V stage j % 2.
-    // One barrier per step.  Slot use per step j: QK_j reads K stage j % 2
-    // (filled in step j - 1); PV_{j-1} reads V stage (j-1) % 2 (filled in step
-    // j - 1) and P slot (j-1) % 2 (written in step j - 1); step j writes K
-    // stage (j+1) % 2 (last read in step j - 1), V stage j % 2 (last read in
-    // step j - 1) and P slot j % 2 (last read in step j - 1).  Every operand
-    // reaches the same MFMA and VALU operations as in the other schedules, so
-    // the bits are the same.
+    // both, and publishes P_j^T and (alpha_j, m_j, l_j) in P slot j % 2.  Step j
+    // runs the softmax of block j, issues S_{j+1} on the matrix cores first so
+    // that it overlaps that softmax, and applies block j - 1 to the output: the
+    // score wave to tiles [0, kPairTilesS), the PV wave, which reads P_{j-1} from
+    // its slot, to the other kPairTilesV.  The PV waves do all the staging
+    // through registers, in two register sets used on alternate steps: step j
+    // loads K_{j+3} and V_{j+1} into set (j+1) % 2, then writes K_{j+2} into K
+    // stage (j+2) % 3 and V_j, widened to bf16, into V stage j % 2 from set
+    // j % 2 (loaded in step j - 1, so a load has a whole step to arrive).
+    // Slot use in step j: K stage (j+1) % 3 is read (written in step j - 1) and
+    // K stage (j+2) % 3 written (last read in step j - 2); V stage (j-1) % 2 read
+    // (written in step j - 1), V stage j % 2 written (last read in step j - 1);
+    // P slot (j-1) % 2 read (written in step j - 1), P slot j % 2 written (last
+    // read in step j - 1).  One barrier per step, which completes the step's
+    // LDS writes but leaves its loads in flight (barrier_lds).  The step loop is
+    // unrolled by two so that the register sets are fixed in the code.  Every
+    // operand reaches the same MFMA and VALU operations as in the other
+    // schedules, so the bits are the same.
     constexpr int NTS = C::kPairTilesS, NTV = C::kPairTilesV;
-    constexpr int kVChunks = kBlockKeys * G::kChunks16;  // 16-byte chunks of a V block
-    constexpr int kVPer = (kVChunks + 255) / 256;         // per PV-wave thread
+    constexpr int kChunks = kBlockKeys * G::kChunks16;  // 16-byte chunks of a K or V block
+    constexpr int kPer = (kChunks + 255) / 256;          // per PV-wave thread
     const int wv = uniform(wave);
     const bool score = wv < 4;
     const int qgp = wv & 3;
     const int dtp = score ? 0 : NTS;  // first output tile of this wave
-    unsigned char* const sP = smem + C::kPOff;
+    unsigned char* const sKp = smem + C::kPcKOff;
+    unsigned char* const sVp = smem + C::kPcVOff;
+    unsigned char* const sP = smem + C::kPcPOff;
     auto pslot = [&](int j) { return sP + ((j & 1) * C::kQGroups + qgp) * C::kPSlot; };
+    auto kstage = [&](int j) { return sKp + (j % C::kPcKStages) * C::kKStage; };
     const float c = p.c_scale;
     // The two roles run separate instantiations of the step loop, so each
     // holds only its own accumulators and running totals in registers.
@@ -615,8 +633,6 @@ void prefill_kernel(const PrefillParams p) {
         const unsigned char* qb = static_cast<const unsigned char*>(p.q) + q_head * G::kRowBytes;
         const unsigned char* kb = static_cast<const unsigned char*>(p.k) + kv_head * G::kRowBytes;
         const unsigned char* vb = static_cast<const unsigned char*>(p.v) + kv_head * G::kRowBytes;
-        const rsrc_t qr = make_rsrc(qb, extent_bytes(nrows, q_row_bytes, G::kRowBytes,
-                                                     (p.total_q * p.hq - q_head) * G::kRowBytes));
         // Window-sized K/V descriptors over key rows [kstart, kend).
         const uint32_t kv_ext =
             extent_bytes(kend - kstart, kv_row_bytes, G::kRowBytes,
@@ -624,79 +640,48 @@ void prefill_kernel(const PrefillParams p) {
         const int64_t kv_win = (int64_t)kstart * kv_row_bytes;
         const rsrc_t kr = make_rsrc(kb + kv_win, kv_ext);
         const rsrc_t vr = make_rsrc(vb + kv_win, kv_ext);
-        // PV waves: direct K staging over their four waves, V through registers.
-        DirectStager<D, 4, true> kst;
-        const int vt = tid - 256;  // PV-wave thread index
-        u32x4 vreg[kVPer];
-        auto v_load = [&](int blk) {
+        if constexpr (S) {
+          // Score wave: its lane's Q^T operands straight from HBM (rows past
+          // the sequence read as zeros), S_0, then the step loop.
+          const rsrc_t qr = make_rsrc(qb, extent_bytes(nrows, q_row_bytes, G::kRowBytes,
+                                                       (p.total_q * p.hq - q_head) * G::kRowBytes));
+          QOperands<D, true> qop;
+          const uint32_t qoff = (uint32_t)(r0 + 32 * qgp + (lane & 31)) * q_row_bytes;
 #pragma unroll
-          for (int u = 0; u < kVPer; ++u) {
-            const int x = vt + 256 * u;
-            if (kVPer * 256 == kVChunks || x < kVChunks) {
-              const int r = x / G::kChunks16, col = x % G::kChunks16;
-              vreg[u] = buf_load16(vr, (uint32_t)((int64_t)(blk * kBlockKeys - kstart + r) * kv_row_bytes) +
-                                           (uint32_t)col * 16u);
-            }
-          }
-        };
-        auto v_store = [&](unsigned char* vs) {
-#pragma unroll
-          for (int u = 0; u < kVPer; ++u) {
-            const int x = vt + 256 * u;
-            if (kVPer * 256 == kVChunks || x < kVChunks) {
-              const int r = x / G::kChunks16, col = x % G::kChunks16;
-              const u32x2 a = e4m3x4_to_bf16x4(vreg[u][0]), b2 = e4m3x4_to_bf16x4(vreg[u][1]);
-              const u32x2 c2 = e4m3x4_to_bf16x4(vreg[u][2]), d2 = e4m3x4_to_bf16x4(vreg[u][3]);
-              const uint32_t o = (uint32_t)(r * G::kVRow + col * 32);
-              lds_store16(vs, o, u32x4{a[0], a[1], b2[0], b2[1]});
-              lds_store16(vs, o + 16, u32x4{c2[0], c2[1], d2[0], d2[1]});
-            }
-          }
-        };
-        // Prologue: K_0 into K stage 0 and V_0 into registers (PV waves), the
-        // Q tile into LDS (every wave), then the score wave's Q^T operands.
-        if constexpr (!S) {
-          kst.init(wv - 4, lane, kr, vr, kv_row_bytes, kstart);
-          kst.issue_k(blk_begin, sK, wv - 4);
-          v_load(blk_begin);
-        }
-        for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
-          const int r = x / G::kChunks16, col = x % G::kChunks16;
-          lds_store16(sQ, (uint32_t)(r * G::kQRow + col * 16),
-                      buf_load16(qr, (uint32_t)(r0 + r) * q_row_bytes + (uint32_t)col * 16u));
-        }
-        wait_vm();
-        __syncthreads();
-        QOperands<D, true> qop;
-        if constexpr (S) qop.load(sQ + (32 * qgp + (lane & 31)) * G::kQRow, lane);
-        u32x4 pb_prev[4] = {};
-        float alpha_prev = 1.0f;
-        for (int j = 0; j <= n; ++j) {
-          const int blk = blk_begin + j;
-          // Block j - 1 is the last block of its chunk (or of the range).
-          const bool chunk_end = j > 0 && (blk % kBlocksPerChunk == 0 || j == n);
-          const bool live_prev = j > 0 && wave_live(blk - 1);
-          if constexpr (S) {
+          for (int st = 0; st < QOperands<D, true>::kCount; ++st)
+            qop.q[st] = buf_load16(qr, qoff + (uint32_t)(64 * (st >> 1) + 32 * h + 16 * (st & 1)));
+          wait_vm();
+          __syncthreads();  // K_0 and K_1 are in their stages
+          f32x16 sc[2][2];  // scores of blocks j (set j % 2) and j + 1
+          if (wave_live(blk_begin)) qk_scores_qreg<D, true, C::kKPage>(sc[0], qop, kstage(0), lane);
+          u32x4 pb_prev[4] = {};
+          float alpha_prev = 1.0f;
+          auto step = [&](int j, auto set) {
+            constexpr int X = decltype(set)::value;
+            const int blk = blk_begin + j;
+            // Block j - 1 is the last block of its chunk (or of the range).
+            const bool chunk_end = j > 0 && (blk % kBlocksPerChunk == 0 || j == n);
             const float mc = m, lc = l;
             if (chunk_end && j < n) {  // block j opens a new chunk from the empty state
               m = -INFINITY;
               l = 0.0f;
             }
+            if (j + 1 < n && wave_live(blk + 1))
+              qk_scores_qreg<D, true, C::kKPage>(sc[X ^ 1], qop, kstage(j + 1), lane);
             u32x4 pb[4];
             float alpha = 1.0f;
             if (j < n && wave_live(blk)) {
-              f32x16 sc[2];
-              qk_scores_qreg<D, true, C::kKPage>(sc, qop, sK + (j & 1) * C::kKStage, lane);
-              softmax(blk, sc, alpha, pb);
+              softmax(blk, sc[X], alpha, pb);
               unsigned char* const ps = pslot(j);
 #pragma unroll
               for (int k = 0; k < 4; ++k) lds_store16(ps, (uint32_t)(k * C::kPRow + lane * 16), pb[k]);
-              lds_store16(ps, (uint32_t)(4 * C::kPRow + lane * 16),
-                          u32x4{f32_bits(alpha), f32_bits(m), f32_bits(l), 0u});
+              if (h == 0)
+                lds_store16(ps, (uint32_t)(4 * C::kPRow + lane * 16),
+                            u32x4{f32_bits(alpha), f32_bits(m), f32_bits(l), 0u});
             }
-            if (live_prev) {
+            if (j > 0 && wave_live(blk - 1)) {
               rescale_acc<NTX>(acc, alpha_prev);
-              pv_mfma<D, NTX>(acc, 0, pb_prev, sV + ((j - 1) & 1) * C::kVStage, lane);
+              pv_mfma<D, NTX>(acc, 0, pb_prev, sVp + ((j - 1) & 1) * C::kVStage, lane);
             }
             if constexpr (!SPLIT) {
               if (chunk_end) fold(mc, lc);
@@ -704,22 +689,87 @@ void prefill_kernel(const PrefillParams p) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) pb_prev[k] = pb[k];
             alpha_prev = alpha;
-          } else {
-            if (j < n) v_store(sV + (j & 1) * C::kVStage);
-            if (j + 1 < n) {
-              kst.issue_k(blk + 1, sK + ((j + 1) & 1) * C::kKStage, wv - 4);
-              v_load(blk + 1);
+            barrier_lds();
+          };
+          int j = 0;
+          for (; j + 1 <= n; j += 2) {
+            step(j, std::integral_constant<int, 0>{});
+            step(j + 1, std::integral_constant<int, 1>{});
+          }
+          if (j <= n) step(j, std::integral_constant<int, 0>{});
+        } else {
+          // PV wave: K and V through registers (two sets), K two blocks
+          // ahead of its use and V one.
+          const int vt = tid - 256;  // PV-wave thread index
+          u32x4 kreg[2][kPer], vreg[2][kPer];
+          auto load = [&](const rsrc_t& r, int blk, u32x4 (&dst)[kPer]) {
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+              const int x = vt + 256 * u;
+              if (kPer * 256 == kChunks || x < kChunks) {
+                const int rr = x / G::kChunks16, col = x % G::kChunks16;
+                dst[u] = buf_load16(r, (uint32_t)((int64_t)(blk * kBlockKeys - kstart + rr) * kv_row_bytes) +
+                                           (uint32_t)col * 16u);
+              }
             }
-            if (live_prev) {
+          };
+          auto k_store = [&](unsigned char* ks, const u32x4 (&src)[kPer]) {
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+              const int x = vt + 256 * u;
+              if (kPer * 256 == kChunks || x < kChunks) {
+                const int rr = x / G::kChunks16, col = x % G::kChunks16;
+                lds_store16(ks, (uint32_t)(rr * G::kKRow + col * 16), src[u]);
+              }
+            }
+          };
+          auto v_store = [&](unsigned char* vs, const u32x4 (&src)[kPer]) {
+#pragma unroll
+            for (int u = 0; u < kPer; ++u) {
+              const int x = vt + 256 * u;
+              if (kPer * 256 == kChunks || x < kChunks) {
+                const int rr = x / G::kChunks16, col = x % G::kChunks16;
+                const u32x2 a = e4m3x4_to_bf16x4(src[u][0]), b2 = e4m3x4_to_bf16x4(src[u][1]);
+                const u32x2 c2 = e4m3x4_to_bf16x4(src[u][2]), d2 = e4m3x4_to_bf16x4(src[u][3]);
+                const uint32_t o = (uint32_t)(rr * G::kVRow + col * 32);
+                lds_store16(vs, o, u32x4{a[0], a[1], b2[0], b2[1]});
+                lds_store16(vs, o + 16, u32x4{c2[0], c2[1], d2[0], d2[1]});
+              }
+            }
+          };
+          // Prologue: K_0 and K_1 into their stages; K_2 and V_0 into set 0.
+          load(kr, blk_begin, kreg[0]);
+          load(kr, blk_begin + 1, kreg[1]);
+          k_store(kstage(0), kreg[0]);
+          k_store(kstage(1), kreg[1]);
+          load(kr, blk_begin + 2, kreg[0]);
+          load(vr, blk_begin, vreg[0]);
+          wait_vm();
+          __syncthreads();  // K_0 and K_1 are in their stages
+          auto step = [&](int j, auto set) {
+            constexpr int X = decltype(set)::value;
+            const int blk = blk_begin + j;
+            const bool chunk_end = j > 0 && (blk % kBlocksPerChunk == 0 || j == n);
+            // Loads of this step into the other set, then the stores of the
+            // blocks loaded in the previous step.  They run in every step, also
+            // past the last block (rows past the descriptors read as zeros, and
+            // those stages are not read in this step), so that every step has
+            // the same count of loads in flight and the waits before the stores
+            // leave this step's loads outstanding.
+            load(kr, blk + 3, kreg[X ^ 1]);
+            load(vr, blk + 1, vreg[X ^ 1]);
+            k_store(kstage(j + 2), kreg[X]);
+            v_store(sVp + X * C::kVStage, vreg[X]);
+            if (j > 0 && wave_live(blk - 1)) {
               const unsigned char* const ps = pslot(j - 1);
               u32x4 pb[4];
 #pragma unroll
               for (int k = 0; k < 4; ++k) pb[k] = lds_load16(ps, (uint32_t)(k * C::kPRow + lane * 16));
-              const u32x4 st = lds_load16(ps, (uint32_t)(4 * C::kPRow + lane * 16));
+              const u32x4 st = lds_load16(ps, (uint32_t)(4 * C::kPRow + (lane & 31) * 16));
               m = bits_f32(st[1]);
               l = bits_f32(st[2]);
               rescale_acc<NTX>(acc, bits_f32(st[0]));
-              pv_mfma<D, NTX>(acc, NTS, pb, sV + ((j - 1) & 1) * C::kVStage, lane);
+              pv_mfma<D, NTX>(acc, NTS, pb, sVp + (X ^ 1) * C::kVStage, lane);
             }
             if constexpr (!SPLIT) {
               if (chunk_end) {
@@ -728,9 +778,15 @@ void prefill_kernel(const PrefillParams p) {
                 l = 0.0f;
               }
             }
+            barrier_lds();
+          };
+          int j = 0;
+          for (; j + 1 <= n; j += 2) {
+            step(j, std::integral_constant<int, 0>{});
+            step(j + 1, std::integral_constant<int, 1>{});
           }
-          wait_vm();
-          __syncthreads();
+          if (j <= n) step(j, std::integral_constant<int, 0>{});
+          wait_vm();  // nothing is left in flight past the loop
         }
       }
       // Epilogue: each wave stores its own output tiles.
