@@ -88,7 +88,9 @@ size_t attn_partials_bytes(int64_t rows, int32_t num_heads_q, int32_t max_chunks
 
 /*
  * Prefill / full-sequence forward / extend over packed variable-length
- * sequences.
+ * sequences (RL-Kernel page, section 2: one chunked arithmetic path for
+ * full-sequence forward and prefill; head_dim 192 with E4M3FN inputs is the
+ * ffpa-attn page's fp8 D=192 case, "Root cause" and "Verification").
  *   q        [total_q, Hq, D]   bf16 or E4M3FN codes
  *   k, v     [total_k, Hkv, D]  bf16 or E4M3FN codes
  *   cu_seqlens_q, cu_seqlens_k  device int32 [batch + 1] exclusive prefix sums;
@@ -116,7 +118,9 @@ da_status attn_prefill_fwd(int32_t dtype, const void* q, const void* k, const vo
                            size_t partials_bytes, void* stream);
 
 /*
- * Single-token decode over a paged KV cache: sequence b's query (row b of q) is
+ * Single-token decode over a paged KV cache (RL-Kernel page, section 2:
+ * single-token paged decode on the same arithmetic path, so a decode row
+ * equals the last prefill row): sequence b's query (row b of q) is
  * the last token of a sequence of context_lens[b] tokens, so every cached key
  * j < context_lens[b] is visible (j >= context_lens[b] - 1 - window_left as well
  * when window_left >= 0; pages wholly below that are not read).  Token j of sequence b lives in page
@@ -181,7 +185,9 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
                                 float* partials, size_t partials_bytes, void* stream);
 
 /*
- * Fold chunk partials into O: for every (row, head), partials c = 0 .. max_chunks-1
+ * Fold chunk partials into O (RL-Kernel page, section 2: chunk partials merged
+ * in ascending order with the exact FlashAttention-2 max/sum rescale, one bf16
+ * rounding at the end): for every (row, head), partials c = 0 .. max_chunks-1
  * are merged left to right with the exact max/sum rescale (empty partials,
  * m = -inf, are skipped), then O = A / L (0 when L = 0) times v_descale is
  * rounded once to bf16.  o [rows, Hq, D] bf16, lse [rows, Hq] fp32 or NULL.
