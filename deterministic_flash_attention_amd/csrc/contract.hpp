@@ -29,16 +29,21 @@
 //     chunk order with the exact max/sum rescale (a skipped empty partial, a
 //     copy into an empty total, or M' = max(M, m_c), a = exp2(M - M'),
 //     b = exp2(m_c - M'), L = L*a + l_c*b, A = A*a + acc_c*b);
-//   * O = L > 0 ? A / L : 0 (IEEE division) times v_descale, plus +0 (which
-//     turns a -0 into +0 and leaves every other value as it is), rounded once
-//     to bf16.
+//   * O = A / L rounded to nearest (0 for a row with no visible key, L = 0),
+//     times v_descale, plus +0 (which turns a -0 into +0 and leaves every other
+//     value as it is), rounded once to bf16.  The quotient is formed from the
+//     row's correctly rounded reciprocal r = 1 / L (one IEEE division per row)
+//     and one remainder correction per element, q0 = A r, e = fma(-q0, L, A),
+//     q = fma(e, r, q0): by Markstein's theorem (r within half an ulp of 1/L,
+//     q0 within an ulp of A/L, the remainder e exact) q is the correctly
+//     rounded A / L whenever the quotient is a normal number.
 //
 // All code is built with -ffp-contract=off: the compiler fuses no multiply-add.
-// The op sequence holds exactly three fused multiply-adds, written explicitly
+// The op sequence holds exactly five fused multiply-adds, written explicitly
 // and run identically by every kernel: p = exp2(fma(s, c, -m')) in the block
-// update, and L = fma(L, a, l_c * b) and A = fma(A, a, acc_c * b) in the chunk
-// fold.  Every other product and sum above is a separately rounded fp32
-// operation.
+// update, L = fma(L, a, l_c * b) and A = fma(A, a, acc_c * b) in the chunk
+// fold, and the two of the finalize correction.  Every other product and sum
+// above is a separately rounded fp32 operation.
 //
 // "Untouched" holds up to the sign of zero: a fully masked block leaves m and
 // l bit for bit, and acc too except that an accumulator element that is -0
@@ -344,11 +349,22 @@ __device__ __forceinline__ float merge_elem(float A, float acc, bool keep, float
   return keep ? A : __builtin_fmaf(A, ca, acc * cb);
 }
 
-__device__ __forceinline__ float finalize_elem(float A, float L, float v_descale) {
-  const float o = (L > 0.0f) ? (A / L) : 0.0f;
-  // x + 0 is x for every x except -0, which becomes +0 (round to nearest even).
-  return o * v_descale + 0.0f;
-}
+// Finalisation of one row (L >= 1 once any key was visible, else L = 0 and
+// A = +0).  UNIT skips the v_descale product, which is exact when v_descale
+// is 1 (bf16 inputs), so both forms give the same bits there.
+struct RowFinal {
+  float L, r, vd;
+  __device__ __forceinline__ RowFinal(float L_, float v_descale)
+      : L(L_), r(L_ > 0.0f ? 1.0f / L_ : 0.0f), vd(v_descale) {}
+  template <bool UNIT = false>
+  __device__ __forceinline__ float elem(float A) const {
+    const float q0 = A * r;
+    const float e = __builtin_fmaf(-q0, L, A);  // exact remainder A - q0 L
+    const float q = __builtin_fmaf(e, r, q0);   // RN(A / L); +0 when L = 0
+    // x + 0 is x for every x except -0, which becomes +0 (round to nearest even).
+    return (UNIT ? q : q * vd) + 0.0f;
+  }
+};
 // Natural-log sum of exp(scale * q.k): M is kept in log2 units.
 __device__ __forceinline__ float finalize_lse(float M, float L) {
   return (L > 0.0f) ? (M + __builtin_amdgcn_logf(L)) * 0.693147180559945309f : -INFINITY;

@@ -303,14 +303,14 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
   if constexpr (!SPLIT) {
     const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + row_head * D * 2,
                                  (uint32_t)grp * D * 2u);
-    const float vd = p.v_descale;
+    const RowFinal fin(L, p.v_descale);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d = 32 * wave + 8 * q4 + 4 * h;
-      const uint32_t w0 = pack_bf16x2(finalize_elem(A[0][4 * q4 + 0], L, vd),
-                                      finalize_elem(A[0][4 * q4 + 1], L, vd));
-      const uint32_t w1 = pack_bf16x2(finalize_elem(A[0][4 * q4 + 2], L, vd),
-                                      finalize_elem(A[0][4 * q4 + 3], L, vd));
+      const uint32_t w0 = pack_bf16x2(fin.elem<!FP8>(A[0][4 * q4 + 0]),
+                                      fin.elem<!FP8>(A[0][4 * q4 + 1]));
+      const uint32_t w1 = pack_bf16x2(fin.elem<!FP8>(A[0][4 * q4 + 2]),
+                                      fin.elem<!FP8>(A[0][4 * q4 + 3]));
       buf_store8(orr, (uint32_t)(n * D + d) * 2u, u32x2{w0, w1});
     }
     if (p.lse != nullptr) {

@@ -87,9 +87,9 @@ __global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(const MergePara
   const int64_t base = valid ? rh : 0;
   const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + base * D * 2,
                                valid ? (uint32_t)(D * 2) : 0u);
+  const RowFinal fin(L, p.v_descale);
 #pragma unroll
-  for (int k = 0; k < PER; ++k)
-    buf_store2(orr, (uint32_t)(lane + 64 * k) * 2u, bf16_bits(finalize_elem(A[k], L, p.v_descale)));
+  for (int k = 0; k < PER; ++k) buf_store2(orr, (uint32_t)(lane + 64 * k) * 2u, bf16_bits(fin.elem(A[k])));
   if (p.lse != nullptr) {
     const rsrc_t lr = make_rsrc(p.lse + base, valid ? 4u : 0u);
     buf_store4(lr, lane == 0 ? 0u : kParked, f32_bits(finalize_lse(M, L)));

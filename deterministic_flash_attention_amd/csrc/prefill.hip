@@ -368,7 +368,8 @@ __device__ __forceinline__ void store_partial(const PrefillParams& p, const f32x
 
 // Monolithic epilogue: O = A / L (times v_descale) for output tiles
 // [dt0, dt0 + NT) rounded once to bf16, and lse from the wave holding tile 0.
-template <int D, int NT>
+// UNIT: bf16 inputs, whose v_descale is 1.
+template <int D, int NT, bool UNIT>
 __device__ __forceinline__ void store_output(const PrefillParams& p, const f32x16 (&A)[NT],
                                              float M, float L, int dt0, int64_t q_start, int head,
                                              int nrows, int64_t rs, int qrow, int h) {
@@ -377,16 +378,16 @@ __device__ __forceinline__ void store_output(const PrefillParams& p, const f32x1
                                extent_bytes(nrows, rs * D * 2, D * 2,
                                             (p.total_q * p.hq - o_head) * D * 2));
   const uint32_t rowoff = (uint32_t)qrow * (uint32_t)(rs * D * 2);
-  const float vd = p.v_descale;
+  const RowFinal fin(L, p.v_descale);
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d = 32 * (dt0 + j) + 8 * q4 + 4 * h;
-      const uint32_t w0 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 0], L, vd),
-                                      finalize_elem(A[j][4 * q4 + 1], L, vd));
-      const uint32_t w1 = pack_bf16x2(finalize_elem(A[j][4 * q4 + 2], L, vd),
-                                      finalize_elem(A[j][4 * q4 + 3], L, vd));
+      const uint32_t w0 = pack_bf16x2(fin.elem<UNIT>(A[j][4 * q4 + 0]),
+                                      fin.elem<UNIT>(A[j][4 * q4 + 1]));
+      const uint32_t w1 = pack_bf16x2(fin.elem<UNIT>(A[j][4 * q4 + 2]),
+                                      fin.elem<UNIT>(A[j][4 * q4 + 3]));
       buf_store8(orr, rowoff + (uint32_t)d * 2u, u32x2{w0, w1});
     }
   if (p.lse != nullptr) {
@@ -793,7 +794,7 @@ void prefill_kernel(const PrefillParams p) {
       if constexpr (SPLIT) {
         store_partial<D, NTX>(p, acc, m, l, dtp, chunk, q_start, head, nrows, rs, qrow, h);
       } else {
-        store_output<D, NTX>(p, A, M, L, dtp, q_start, head, nrows, rs, qrow, h);
+        store_output<D, NTX, !FP8>(p, A, M, L, dtp, q_start, head, nrows, rs, qrow, h);
       }
     };
     if (score) {
@@ -1072,7 +1073,7 @@ void prefill_kernel(const PrefillParams p) {
   if constexpr (SPLIT) {
     store_partial<D, NT>(p, acc, m, l, dt0, chunk, q_start, head, nrows, rs, qrow, h);
   } else {
-    store_output<D, NT>(p, A, M, L, dt0, q_start, head, nrows, rs, qrow, h);
+    store_output<D, NT, !FP8>(p, A, M, L, dt0, q_start, head, nrows, rs, qrow, h);
   }
 }
 
