@@ -264,15 +264,26 @@ def extend_setup():
 
 def extend_line():
     """The mixed prefill / extend / decode batch over a paged cache, one
-    monolithic launch of attn_paged_extend_fwd per step."""
+    monolithic launch of attn_paged_extend_fwd per step, with the workspace
+    that spreads the decode rows' chunks over the launch's idle workgroups
+    (zero-filled once, outside the timed region; every launch leaves its
+    counters at zero).  The same launch without the workspace is timed
+    beside it ("single_tile")."""
     import torch
     import deterministic_flash_attention_amd as dfa
     import oracle
     cfg, inp, t = extend_setup()
     o = torch.empty_like(t["q"])
     mq, mc = max(inp.q_lens), max(inp.ctx_lens)
+    nbytes = dfa.attn_extend_workspace_bytes(len(inp.q_lens), cfg["hq"], cfg["hkv"],
+                                             dfa.attn_num_chunks(mc), cfg["d"])
+    ws = torch.zeros((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
 
     def fn():
+        dfa.attn_paged_extend_fwd(t["q"], t["cq"], t["kc"], t["vc"], t["pt"], t["cl"], mq, mc,
+                                  inp.scale, True, dfa.MONOLITHIC, o=o, partials=ws)
+
+    def fn_single():
         dfa.attn_paged_extend_fwd(t["q"], t["cq"], t["kc"], t["vc"], t["pt"], t["cl"], mq, mc,
                                   inp.scale, True, dfa.MONOLITHIC, o=o)
     flops = oracle.attention_flops(inp.q_lens, inp.ctx_lens, cfg["hq"], cfg["d"], True)
@@ -284,11 +295,14 @@ def extend_line():
             "workload": "mixed_paged_extend", "causal": True, "dtype": "bf16",
             "ctx_lens": inp.ctx_lens, "q_lens": inp.q_lens, "hq": cfg["hq"], "hkv": cfg["hkv"],
             "d": cfg["d"], "flop": flops, **s, "value": tf, "unit": "TFLOP/s",
+            "workspace_bytes": nbytes,
+            "single_tile_ms_median": st["single"]["ms_median"],
+            "single_tile_tflops": flops / (st["single"]["ms_median"] * 1e-3) / 1e12,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
-                         "kernel": "prefill_kernel<128, bf16, paged, monolithic>"},
+                         "kernel": "prefill_kernel<128, bf16, paged, monolithic, chunk spread>"},
         }
-    return Line({"run": fn}, finish)
+    return Line({"run": fn, "single": fn_single}, finish)
 
 
 def gemm_line(name, m, n, k):

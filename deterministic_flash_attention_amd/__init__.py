@@ -2,7 +2,8 @@
 
 The functions named like the C entry points (``attn_prefill_fwd``,
 ``attn_decode_split_fwd``, ``attn_paged_extend_fwd``, ``attn_chunk_merge``,
-``attn_partials_bytes``, ``attn_num_chunks``, ``attn_status_str``, and the GEMM's
+``attn_partials_bytes``, ``attn_extend_workspace_bytes``, ``attn_num_chunks``,
+``attn_status_str``, and the GEMM's
 ``det_gemm_fwd``, ``det_gemm_workspace_bytes``, ``det_gemm_num_chunks``,
 ``det_gemm_num_configs``, ``det_gemm_config_tile``) take torch
 tensors that already live on the GPU, pass their device pointers and sizes to
@@ -25,7 +26,7 @@ import torch
 __all__ = [
     "DetAttnError", "BF16", "FP8_E4M3", "MONOLITHIC", "SPLIT", "BLOCK_KEYS", "CHUNK_KEYS",
     "PAGE_SIZE", "library_path", "load_library", "attn_status_str", "attn_num_chunks",
-    "attn_partials_bytes", "attn_prefill_fwd", "attn_decode_split_fwd", "attn_paged_extend_fwd",
+    "attn_partials_bytes", "attn_extend_workspace_bytes", "attn_prefill_fwd", "attn_decode_split_fwd", "attn_paged_extend_fwd",
     "attn_chunk_merge", "attn_decode_fwd_noalloc", "DECODE_SCRATCH_BYTES", "prefill", "decode",
     "paged_extend", "WEIGHT_NK", "WEIGHT_KN",
     "GEMM_BLOCK_K", "GEMM_CHUNK_K", "det_gemm_num_chunks", "det_gemm_workspace_bytes",
@@ -71,6 +72,8 @@ def load_library() -> ctypes.CDLL:
     lib.attn_num_chunks.restype = c_i32
     lib.attn_partials_bytes.argtypes = [c_i64, c_i32, c_i32, c_i32]
     lib.attn_partials_bytes.restype = c_sz
+    lib.attn_extend_workspace_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32, c_i32]
+    lib.attn_extend_workspace_bytes.restype = c_sz
     lib.attn_prefill_fwd.argtypes = [c_i32, c_p, c_p, c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i64,
                                      c_i64, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_i32,
                                      c_f32, c_f32, c_f32, c_i32, c_p, c_p, c_p, c_sz, c_p]
@@ -148,6 +151,13 @@ def attn_partials_bytes(rows: int, num_heads_q: int, max_chunks: int, head_dim: 
                                                   int(head_dim)))
 
 
+def attn_extend_workspace_bytes(batch: int, num_heads_q: int, num_heads_kv: int,
+                                max_chunks: int, head_dim: int) -> int:
+    return int(load_library().attn_extend_workspace_bytes(int(batch), int(num_heads_q),
+                                                          int(num_heads_kv), int(max_chunks),
+                                                          int(head_dim)))
+
+
 def attn_prefill_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
                      softmax_scale: float, causal: bool, schedule: int = MONOLITHIC,
                      o=None, lse=None, partials=None, descales=(1.0, 1.0, 1.0),
@@ -203,7 +213,10 @@ def attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context
                           partials=None, descales=(1.0, 1.0, 1.0), window=(-1, -1),
                           stream=None, kv_layout: str = "NHD") -> None:
     """Mirror of the C ``attn_paged_extend_fwd`` for contiguous caches in the
-    "NHD" [num_pages, 16, Hkv, D] or "HND" [num_pages, Hkv, 16, D] layout."""
+    "NHD" [num_pages, 16, Hkv, D] or "HND" [num_pages, Hkv, 16, D] layout.
+    ``partials``: the split schedule's chunk partials, or for the monolithic
+    schedule an optional workspace of ``attn_extend_workspace_bytes`` bytes
+    whose counters start at zero (a ``torch.zeros`` buffer)."""
     lib = load_library()
     npages, psize, hkv, d, s_page, s_tok, s_head = _cache_geometry(k_cache, kv_layout)
     st = lib.attn_paged_extend_fwd(
@@ -372,10 +385,11 @@ def paged_extend(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens, ma
                  max_context_len: int, causal: bool, softmax_scale: Optional[float] = None,
                  schedule: int = MONOLITHIC, descales=(1.0, 1.0, 1.0),
                  out: Optional[torch.Tensor] = None, return_lse: bool = False, window=(-1, -1),
-                 stream=None, kv_layout: str = "NHD"):
+                 stream=None, kv_layout: str = "NHD", workspace: Optional[torch.Tensor] = None):
     """Mixed prefill / extend / decode batch over a paged KV cache; returns O
     (bf16) and optionally lse.  Sequence b's rows are its last
-    cu_seqlens_q[b+1] - cu_seqlens_q[b] tokens of context_lens[b]."""
+    cu_seqlens_q[b+1] - cu_seqlens_q[b] tokens of context_lens[b].  ``workspace``
+    (monolithic schedule): see ``attn_paged_extend_fwd``."""
     tq, hq, d = q.shape
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
@@ -392,6 +406,6 @@ def paged_extend(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens, ma
     else:
         attn_paged_extend_fwd(q, cu_seqlens_q, k_cache, v_cache, page_table, context_lens,
                               max_seqlen_q, max_context_len, softmax_scale, causal, MONOLITHIC,
-                              o=o, lse=lse, descales=descales, window=window, stream=stream,
-                              kv_layout=kv_layout)
+                              o=o, lse=lse, partials=workspace, descales=descales, window=window,
+                              stream=stream, kv_layout=kv_layout)
     return (o, lse) if return_lse else o

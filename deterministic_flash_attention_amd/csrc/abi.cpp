@@ -125,6 +125,15 @@ size_t attn_partials_bytes(int64_t rows, int32_t num_heads_q, int32_t max_chunks
   return partials_bytes_or_max(rows, num_heads_q, max_chunks, head_dim);
 }
 
+size_t attn_extend_workspace_bytes(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
+                                   int32_t max_chunks, int32_t head_dim) {
+  if (batch < 0 || num_heads_kv < 0) return 0;
+  const size_t cells = partials_bytes_or_max(batch, num_heads_q, max_chunks, head_dim);
+  if (cells == std::numeric_limits<size_t>::max()) return cells;
+  // The counters: one int32 per (sequence, kv head), after the partials.
+  return cells + (size_t)batch * (size_t)num_heads_kv * 4u;
+}
+
 da_status attn_prefill_fwd(int32_t dtype, const void* q, const void* k, const void* v,
                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                            int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
@@ -229,13 +238,26 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
   if (token_stride * es * DA_PAGE_SIZE > kMaxOffset) return DA_EUNSUPPORTED;
   if (!split && (!o || !aligned(o, 16) || (lse && !aligned(lse, 4)))) return DA_EINVAL;
   if (split && (!partials || !aligned(partials, 16))) return DA_EINVAL;
+  if (!split && partials && !aligned(partials, 16)) return DA_EINVAL;
 
   const int tile = detattn::prefill_tile_rows(head_dim, dtype == DA_FP8_E4M3);
   if (((int64_t)max_seqlen_q + tile) * num_heads_q * head_dim * 4 > kMaxOffset) return DA_EUNSUPPORTED;
-  const int32_t tiles = (int32_t)((max_seqlen_q + tile - 1) / tile);
   const int32_t cmax = chunks_for(max_context_len);
+  int32_t tiles = (int32_t)((max_seqlen_q + tile - 1) / tile);
+  if (!split && partials && max_seqlen_q > 0 &&
+      detattn::paged_extend_spreads(head_dim, dtype == DA_FP8_E4M3)) {
+    // Chunk spread: a single-token sequence's tile set (the query heads of a
+    // kv group, packed in one tile, or one head without grouping) gets a
+    // workgroup slot per chunk; the launch's tile slots grow to that.
+    const int32_t group = num_heads_q / num_heads_kv;
+    const int32_t tset = group > 1 ? group : 1;
+    tiles = std::max(tiles, (cmax + tset - 1) / tset);
+  }
   if ((int64_t)batch * num_heads_q * tiles * (split ? cmax : 1) > kMaxOffset) return DA_EUNSUPPORTED;
   if (split && partials_bytes < partials_bytes_or_max(total_q, num_heads_q, cmax, head_dim))
+    return DA_EWORKSPACE;
+  if (!split && partials &&
+      partials_bytes < attn_extend_workspace_bytes(batch, num_heads_q, num_heads_kv, cmax, head_dim))
     return DA_EWORKSPACE;
   if (batch == 0 || tiles == 0 || (split && cmax == 0)) return DA_OK;
 
@@ -268,6 +290,16 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
   p.token_stride = token_stride;
   p.head_stride = head_stride;
   p.max_pages = max_pages_per_seq;
+  if (!split && partials) {
+    // Monolithic with a workspace: chunk partials of spread single-token
+    // sequences, then their counters.
+    const size_t cells = (size_t)cmax * batch * num_heads_q;
+    p.ws_acc = partials;
+    p.ws_ml = partials + cells * head_dim;
+    p.ws_cnt = reinterpret_cast<int32_t*>(partials + cells * (head_dim + 2));
+    p.part_acc = nullptr;
+    p.part_ml = nullptr;
+  }
   const hipError_t e = detattn::launch_prefill(p, head_dim, dtype == DA_FP8_E4M3, split, true,
                                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DA_OK : DA_ELAUNCH;

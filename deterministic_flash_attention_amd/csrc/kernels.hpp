@@ -37,6 +37,11 @@ struct PrefillParams {
   int64_t token_stride;
   int64_t head_stride;
   int32_t max_pages;
+  // Monolithic paged extend with a workspace: single-token sequences spread
+  // their chunks over workgroups (null: no workspace).
+  float* ws_acc;      // fp32 [cmax, batch, hq, D]
+  float* ws_ml;       // fp32 [cmax, batch, hq, 2]
+  int32_t* ws_cnt;    // int32 [batch, hkv], zero between launches
 };
 
 struct DecodeParams {
@@ -93,6 +98,9 @@ hipError_t launch_decode(const DecodeParams& p, int head_dim, bool fp8, bool spl
                          hipStream_t stream);
 hipError_t launch_merge(const MergeParams& p, int head_dim, hipStream_t stream);
 
+// Whether the monolithic paged extend kernel of this configuration spreads
+// single-token sequences over workgroups when given a workspace.
+bool paged_extend_spreads(int head_dim, bool fp8);
 int prefill_tile_rows(int head_dim, bool fp8);
 
 // GEMM: config selects the tile shape (0 .. gemm_num_configs() - 1); every

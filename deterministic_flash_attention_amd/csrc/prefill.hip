@@ -303,8 +303,10 @@ struct PagedDirectStager {
   // issued next; indices are clamped into the table row (entries of pages
   // without a live token are never used).
   __device__ __forceinline__ void prefetch(int kblk, int vblk) {
-    kent = table[max(0, min(kblk * 4 + page, max_pages - 1))];
-    vent = table[max(0, min(vblk * 4 + page, max_pages - 1))];
+    // One entry per wave (its page): read into scalar registers, so the page
+    // descriptors stay scalar too.
+    kent = uniform(table[max(0, min(kblk * 4 + page, max_pages - 1))]);
+    vent = uniform(table[max(0, min(vblk * 4 + page, max_pages - 1))]);
   }
   // Descriptor of this wave's page of block blk, whose table entry is pg.
   __device__ __forceinline__ rsrc_t page_rsrc(const unsigned char* cache, int blk,
@@ -398,6 +400,13 @@ __device__ __forceinline__ void store_output(const PrefillParams& p, const f32x1
   }
 }
 
+// Configurations whose monolithic paged kernel spreads single-token sequences
+// over workgroups when given a workspace: all but bf16 D = 192, whose four
+// waves hold six output tiles each and have no registers left for the chunk
+// partial's stores.
+template <int D, bool FP8, bool MONO_PAGED>
+constexpr bool kSpread = MONO_PAGED && (FP8 || D <= 128);
+
 template <int D, bool FP8, int NW, int WPE, bool SPLIT, bool PAGED, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void prefill_kernel(const PrefillParams p) {
@@ -484,12 +493,19 @@ void prefill_kernel(const PrefillParams p) {
   // first head computes the tile; the others have nothing to do.
   const int grp_size = p.hq / p.hkv;
   const bool pack = PAGED && lq == 1 && grp_size > 1;
-  if (pack && head % grp_size != 0) return;
+  // With a workspace, a single-token sequence may spread its chunks over the
+  // workgroup slots of its tile set (query heads of the set times the tile
+  // slots of the launch); see the chunk spread below.
+  const bool ds_try = kSpread<D, FP8, PAGED && !SPLIT> && lq == 1 && p.ws_cnt != nullptr;
+  const int tset = pack ? grp_size : 1;                // query heads per tile set
+  const int ds_slot = tile_rev * tset + head % tset;   // this workgroup's slot in the set
+  if (!ds_try && pack && head % grp_size != 0) return;
+  head -= head % tset;  // the tile set's first query head
   const int nrows = pack ? grp_size : lq;  // real rows of this tile set
   const int64_t rs = pack ? 1 : p.hq;      // row stride in head rows
   auto pos = [&](int i) { return pack ? 0 : i; };  // query position of local row i
   const int ntiles = (nrows + C::kTileRows - 1) / C::kTileRows;
-  const int tile = ntiles - 1 - tile_rev;
+  const int tile = ds_try ? 0 : ntiles - 1 - tile_rev;
   if (tile < 0) return;
   const int r0 = tile * C::kTileRows;
   const int g = head / grp_size;
@@ -519,6 +535,38 @@ void prefill_kernel(const PrefillParams p) {
   if constexpr (SPLIT) {
     blk_begin = max(chunk * kBlocksPerChunk, blk_first);
     blk_end = min(chunk * kBlocksPerChunk + kBlocksPerChunk, nblk);
+  }
+  // Chunk spread.  A single-token sequence (a decode row; the query heads of
+  // its group packed in one tile) scans its whole context on one wave, a chain
+  // that outlasts the rest of a mixed batch.  With a workspace, its chunks
+  // [ds_first, ds_first + ds_chunks) are dealt to the first ds_count =
+  // ds_chunks slots of its tile set, one chunk each, from the empty state as
+  // always (the host sizes the launch's tile slots so that every set has a
+  // slot per chunk); every chunk's partial goes to the workspace, and the slot that
+  // completes the set's counter folds them in ascending order and finalises
+  // the rows.  That is the fold the single tile runs in registers, on the same
+  // partials, so the rows keep their bits.  Sets whose chunks would pass the
+  // launch's chunk count (a context length above max_context_len) keep the
+  // single tile.
+  bool dsplit = false;
+  int ds_first = 0, ds_chunks = 0, ds_count = 1;
+  if constexpr (kSpread<D, FP8, PAGED && !SPLIT>) {
+    if (ds_try) {
+      const int cf = blk_first / kBlocksPerChunk;
+      const int cl = nblk > blk_first ? (nblk + kBlocksPerChunk - 1) / kBlocksPerChunk : cf;
+      const int cnt = cl - cf;
+      if (cnt > 1 && cnt <= tset * p.tiles && cl <= p.cmax) {
+        if (ds_slot >= cnt) return;
+        dsplit = true;
+        ds_first = cf;
+        ds_chunks = cnt;
+        ds_count = cnt;
+        blk_begin = max(blk_first, (cf + ds_slot) * kBlocksPerChunk);
+        blk_end = min(nblk, (cf + ds_slot + 1) * kBlocksPerChunk);
+      } else if (ds_slot != 0) {
+        return;
+      }
+    }
   }
 
   // Query group (32 rows) and output columns [32 dt0, 32 (dt0 + NT)) of this wave.
@@ -829,6 +877,57 @@ void prefill_kernel(const PrefillParams p) {
     }
   };
 
+  // The end of a chunk inside the block loop folds its partial into the
+  // running total; the end of the loop (chunk c) does the same, or, when the
+  // chunk spread deals this tile set's chunks out, stores the partial in the
+  // workspace (the wave's rows and output tiles; one lane per row for (m, l)).
+  // The accumulator restarts from +0 either way.
+  auto fold_chunk = [&]() {
+    float ca, cb;
+    bool keep;
+    merge_stats(M, L, m, l, ca, cb, keep);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        A[t][i] = merge_elem(A[t][i], acc[t][i], keep, ca, cb);
+        acc[t][i] = 0.0f;
+      }
+    m = -INFINITY;
+    l = 0.0f;
+  };
+  auto end_chunk = [&](int c) {
+    if (kSpread<D, FP8, PAGED && !SPLIT> && dsplit) {
+      const int64_t slot = ((int64_t)c * p.batch + b) * p.hq + head;
+      const rsrc_t mlr = make_rsrc(p.ws_ml + 2 * slot, (uint32_t)nrows * 8u);
+      buf_store8(mlr, (h || dt0) ? kParked : (uint32_t)qrow * 8u, u32x2{f32_bits(m), f32_bits(l)});
+      const rsrc_t ar = make_rsrc(p.ws_acc + slot * D, (uint32_t)nrows * D * 4u);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = 32 * (dt0 + t) + 8 * q4 + 4 * h;
+          buf_store16(ar, (uint32_t)(qrow * D + d) * 4u,
+                      u32x4{f32_bits(acc[t][4 * q4 + 0]), f32_bits(acc[t][4 * q4 + 1]),
+                            f32_bits(acc[t][4 * q4 + 2]), f32_bits(acc[t][4 * q4 + 3])});
+        }
+    } else {
+      float ca, cb;
+      bool keep;
+      merge_stats(M, L, m, l, ca, cb, keep);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) A[t][i] = merge_elem(A[t][i], acc[t][i], keep, ca, cb);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+    m = -INFINITY;
+    l = 0.0f;
+  };
+
   if (blk_begin < blk_end) {
     const int64_t q_head = (int64_t)q_start * p.hq + head;
     const int64_t kv_head = (int64_t)k_start * p.hkv + g;
@@ -922,20 +1021,6 @@ void prefill_kernel(const PrefillParams p) {
     // bf16: the wave's Q^T operands move from the LDS tile to registers once.
     QOperands<D, FP8> qop;
     if constexpr (!FP8) qop.load(sQw + (lane & 31) * G::kQRow, lane);
-    auto fold_chunk = [&]() {
-      float ca, cb;
-      bool keep;
-      merge_stats(M, L, m, l, ca, cb, keep);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          A[t][i] = merge_elem(A[t][i], acc[t][i], keep, ca, cb);
-          acc[t][i] = 0.0f;
-        }
-      m = -INFINITY;
-      l = 0.0f;
-    };
     u32x4 pb[4];
     for (int j = 0; j < n; ++j) {
       const int blk = blk_begin + j;
@@ -967,7 +1052,7 @@ void prefill_kernel(const PrefillParams p) {
       __syncthreads();
     }
     if (wave_live(blk_end - 1)) pv_mfma<D, NT>(acc, dt0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
-    if constexpr (!SPLIT) fold_chunk();
+    if constexpr (!SPLIT) end_chunk((blk_end - 1) / kBlocksPerChunk);
     if (!lag) __syncthreads();
       } else {
     const int n = blk_end - blk_begin;
@@ -1040,21 +1125,7 @@ void prefill_kernel(const PrefillParams p) {
         pv_accumulate<D, NT>(acc, dt0, alpha, pb, sV + cur * C::kVStage, lane);
       }
       if constexpr (!SPLIT) {
-        if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) {
-          // End of a 512-key chunk: fold its partial into the running total.
-          float ca, cb;
-          bool keep;
-          merge_stats(M, L, m, l, ca, cb, keep);
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              A[t][i] = merge_elem(A[t][i], acc[t][i], keep, ca, cb);
-              acc[t][i] = 0.0f;
-            }
-          m = -INFINITY;
-          l = 0.0f;
-        }
+        if ((blk + 1) % kBlocksPerChunk == 0 && more) fold_chunk();
       }
       if (more) {
         if constexpr (C::kDirect) {
@@ -1067,9 +1138,66 @@ void prefill_kernel(const PrefillParams p) {
       }
       __syncthreads();
     }
+    if constexpr (!SPLIT) end_chunk((blk_end - 1) / kBlocksPerChunk);
       }
   }
 
+  if constexpr (kSpread<D, FP8, PAGED && !SPLIT>) {
+    if (dsplit) {
+      // Count this workgroup in (its partial stores made visible at device
+      // scope first); the one that completes the set's count folds every chunk
+      // partial in ascending order, finalises the rows and clears the counter
+      // for the next launch.
+      __shared__ int sLast;
+      __syncthreads();
+      int32_t* const cnt = p.ws_cnt + (int64_t)b * p.hkv + g;
+      if (tid == 0) {
+        __threadfence();
+        const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        sLast = done == ds_count - 1 ? 1 : 0;
+        if (sLast) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (!sLast) return;
+      __threadfence();
+      const int64_t o_head = (int64_t)q_start * p.hq + head;
+      const rsrc_t orr = make_rsrc(static_cast<unsigned char*>(p.o) + o_head * D * 2,
+                                   (uint32_t)nrows * D * 2u);
+      const rsrc_t lr = make_rsrc(p.lse != nullptr ? p.lse + o_head : nullptr,
+                                  p.lse != nullptr ? (uint32_t)nrows * 4u : 0u);
+      // The partials are read kBatch chunks at a time (all loads issued before
+      // the first fold), so the fold waits on one memory round trip per batch.
+      constexpr int kBatch = 16;
+      const int cend = ds_first + ds_chunks;
+      for (int e = tid; e < nrows * D; e += C::kThreads) {
+        const int r = e / D, d = e % D;
+        float Mx = -INFINITY, Lx = 0.0f, Ax = 0.0f;
+        for (int c0 = ds_first; c0 < cend; c0 += kBatch) {
+          float mv[kBatch], lv[kBatch], av[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int64_t slot = ((int64_t)min(c0 + u, cend - 1) * p.batch + b) * p.hq + head + r;
+            mv[u] = p.ws_ml[2 * slot];
+            lv[u] = p.ws_ml[2 * slot + 1];
+            av[u] = p.ws_acc[slot * D + d];
+          }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            if (c0 + u < cend) {
+              float ca, cb;
+              bool keep;
+              merge_stats(Mx, Lx, mv[u], lv[u], ca, cb, keep);
+              Ax = merge_elem(Ax, av[u], keep, ca, cb);
+            }
+          }
+        }
+        const RowFinal fin(Lx, p.v_descale);
+        buf_store2(orr, (uint32_t)e * 2u, bf16_bits(fin.elem<!FP8>(Ax)));
+        if (d == 0) buf_store4(lr, (uint32_t)r * 4u, f32_bits(finalize_lse(Mx, Lx)));
+      }
+      return;
+    }
+  }
   if constexpr (SPLIT) {
     store_partial<D, NT>(p, acc, m, l, dt0, chunk, q_start, head, nrows, rs, qrow, h);
   } else {
@@ -1129,6 +1257,8 @@ hipError_t launch_layout(const PrefillParams& p, bool split, bool paged, hipStre
 }
 
 }  // namespace
+
+bool paged_extend_spreads(int head_dim, bool fp8) { return fp8 || head_dim <= 128; }
 
 int prefill_tile_rows(int head_dim, bool fp8) {
   switch (head_dim) {

@@ -60,14 +60,23 @@ def run_decode(inp: synth.DecodeInputs, schedule: int, return_lse: bool = False,
     return res
 
 
-def run_extend(inp: synth.ExtendInputs, schedule: int, return_lse: bool = False, out=None):
+def extend_workspace(inp: synth.ExtendInputs):
+    """A zero-filled workspace for the monolithic paged extend's chunk spread."""
+    import deterministic_flash_attention_amd as dfa
+    nbytes = dfa.attn_extend_workspace_bytes(len(inp.q_lens), inp.hq, inp.hkv,
+                                             dfa.attn_num_chunks(max(inp.ctx_lens)), inp.d)
+    return torch.zeros((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
+
+
+def run_extend(inp: synth.ExtendInputs, schedule: int, return_lse: bool = False, out=None,
+               workspace=None, window=(-1, -1)):
     """The mixed batch through attn_paged_extend_fwd (plus the merge for SPLIT)."""
     import deterministic_flash_attention_amd as dfa
     res = dfa.paged_extend(dev(inp.q), dev(inp.cu_seqlens_q), dev(inp.k_cache), dev(inp.v_cache),
                            dev(inp.page_table), dev(inp.context_lens), max(inp.q_lens),
                            max(inp.ctx_lens), inp.causal, softmax_scale=inp.scale,
                            schedule=schedule, descales=descales(inp), out=out,
-                           return_lse=return_lse)
+                           return_lse=return_lse, workspace=workspace, window=window)
     torch.cuda.synchronize()
     return res
 

@@ -33,6 +33,7 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     assert names == sorted(["attn_status_str", "attn_num_chunks", "attn_partials_bytes",
+                            "attn_extend_workspace_bytes",
                             "attn_prefill_fwd", "attn_decode_split_fwd",
                             "attn_paged_extend_fwd", "attn_chunk_merge",
                             "attn_decode_fwd_noalloc"])
@@ -54,6 +55,9 @@ def test_small_helpers(lib):
     assert lib.attn_num_chunks(32768) == 64
     assert lib.attn_partials_bytes(8192, 32, 16, 128) == 8192 * 32 * 16 * 130 * 4
     assert lib.attn_partials_bytes(-1, 32, 16, 128) == 0
+    lib.attn_extend_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.attn_extend_workspace_bytes(11, 32, 8, 64, 128) == 11 * 32 * 64 * 130 * 4 + 11 * 8 * 4
+    assert lib.attn_extend_workspace_bytes(-1, 32, 8, 64, 128) == 0
     for s in range(5):
         assert lib.attn_status_str(s).decode().startswith("DA_")
 
@@ -188,6 +192,8 @@ def _extend_args(**over):
     (dict(kd=3.0), DA_EINVAL),                # descales must be 1 for bf16
     (dict(schedule=1, part=None), DA_EINVAL),
     (dict(schedule=1, part=FAKE, part_bytes=4096), DA_EWORKSPACE),
+    (dict(part=FAKE, part_bytes=4096), DA_EWORKSPACE),   # monolithic, workspace too small
+    (dict(part=FAKE + 4, part_bytes=1 << 30), DA_EINVAL),  # monolithic, misaligned workspace
     (dict(max_q=1 << 28), DA_EUNSUPPORTED),   # beyond 32-bit descriptor offsets
     (dict(wl=-7), DA_EINVAL),
     (dict(batch=0), DA_OK),                   # no work: nothing launched

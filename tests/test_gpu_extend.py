@@ -10,8 +10,8 @@ import pytest
 import torch
 
 import synth
-from gpu_utils import (assert_bitwise, compare, dev, note, oracle_extend, run_decode,
-                       run_extend, run_prefill)
+from gpu_utils import (assert_bitwise, compare, dev, extend_workspace, note, oracle_extend,
+                       run_decode, run_extend, run_prefill)
 
 pytestmark = pytest.mark.gpu
 
@@ -137,6 +137,8 @@ def test_full_mixed_workload():
     o = run_extend(inp, MONO)
     o_split = run_extend(inp, SPLIT)
     assert_bitwise(o_split, o, "mixed workload split vs monolithic")
+    o_ws = run_extend(inp, MONO, workspace=extend_workspace(inp))
+    assert_bitwise(o_ws, o, "mixed workload with the chunk-spread workspace vs without")
     note("oracle on every row")
     ref, _ = oracle_extend(inp)
     compare(o, ref, False, label=f"O full mixed extend (all {ref.size} elements)")

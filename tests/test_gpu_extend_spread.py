@@ -1,0 +1,92 @@
+"""Chunk spread of the monolithic paged extend (RL-Kernel page, section 2: a
+mixed batch of prefill, extend and decode sequences goes through one launch).
+Given a workspace, a single-token sequence whose context spans several chunks
+has its chunks computed by otherwise idle workgroups of the same launch, and
+the last of them folds the chunk partials.  Its rows must keep the bits of the
+launch without a workspace (which the extend tests tie to prefill, decode and
+the oracle), call after call, with the workspace's counters back at zero."""
+import pytest
+import torch
+
+import synth
+from gpu_utils import assert_bitwise, compare, extend_workspace, note, oracle_extend, run_extend
+
+pytestmark = pytest.mark.gpu
+
+MONO = 0
+
+# Decode rows of 1 to 10 chunks next to prefill, extend and short decode rows.
+CTX = [300, 5000, 1100, 64, 2000, 3000, 777, 1, 4097]
+QL = [300, 1, 37, 1, 700, 1, 777, 1, 1]
+LONG = 1  # the 5000-token decode row: 10 chunks
+
+
+def _regions(ws, inp):
+    """(ml [cmax, batch, hq, 2], counters [batch, hkv]) views of the workspace."""
+    import deterministic_flash_attention_amd as dfa
+    b, cmax = len(inp.q_lens), dfa.attn_num_chunks(max(inp.ctx_lens))
+    cells = cmax * b * inp.hq
+    ml = ws[cells * inp.d:cells * (inp.d + 2)].view(cmax, b, inp.hq, 2)
+    cnt = ws[cells * (inp.d + 2):].view(torch.int32)[:b * inp.hkv]
+    return ml, cnt
+
+
+def _spread_vs_single(inp, window=(-1, -1), calls=2):
+    o_ref, l_ref = run_extend(inp, MONO, return_lse=True, window=window)
+    ws = extend_workspace(inp)
+    for call in range(calls):
+        o, lse = run_extend(inp, MONO, return_lse=True, workspace=ws, window=window)
+        assert_bitwise(o, o_ref, f"O with workspace (call {call}) vs without")
+        assert_bitwise(lse, l_ref, f"lse with workspace (call {call}) vs without")
+        _, cnt = _regions(ws, inp)
+        assert int(torch.count_nonzero(cnt)) == 0, "counters not back at zero"
+    return o_ref, ws
+
+
+@pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 8, 2), ("bf16", 64, 4, 1),
+                                            ("bf16", 128, 4, 4), ("fp8", 128, 4, 2),
+                                            ("fp8", 192, 4, 4)])
+def test_spread_equals_single_tile(dtype, d, hq, hkv):
+    inp = synth.extend_inputs(61, CTX, QL, hq, hkv, d, dtype=dtype)
+    note(f"chunk spread {dtype} d={d} hq={hq} hkv={hkv} ctx={CTX} q={QL}")
+    _, ws = _spread_vs_single(inp)
+    # The spread ran: every chunk partial of the long decode row's heads is in
+    # the workspace (m finite, l >= 1), and no chunk past its context is.
+    ml, _ = _regions(ws, inp)
+    nch = (CTX[LONG] + 511) // 512
+    m, l = ml[:nch, LONG, :, 0], ml[:nch, LONG, :, 1]
+    assert torch.isfinite(m).all() and (l >= 1.0).all()
+    assert int(torch.count_nonzero(ml[nch:, LONG])) == 0
+
+
+def test_spread_against_oracle():
+    inp = synth.extend_inputs(63, CTX, QL, 8, 2, 128)
+    o, _ = _spread_vs_single(inp, calls=1)
+    ref, _ = oracle_extend(inp)
+    compare(o, ref, False, label="O paged extend with chunk spread")
+
+
+def test_spread_with_left_window():
+    """Decode rows whose window starts inside a chunk: the spread covers the
+    chunks from the window's first one."""
+    inp = synth.extend_inputs(65, CTX, QL, 8, 2, 128)
+    _spread_vs_single(inp, window=(1500, -1))
+
+
+def test_spread_decode_only_batch():
+    """max_seqlen_q = 1: the launch's tile slots are widened so that every
+    decode row has a slot per chunk."""
+    ctx = [1, 700, 4097, 9000, 513]
+    inp = synth.extend_inputs(67, ctx, [1] * len(ctx), 32, 8, 128)
+    _spread_vs_single(inp)
+
+
+def test_no_spread_for_bf16_d192():
+    """bf16 D = 192 runs the single tile with or without a workspace, which
+    then stays untouched."""
+    inp = synth.extend_inputs(69, CTX, QL, 4, 4, 192)
+    o_ref = run_extend(inp, MONO)
+    ws = extend_workspace(inp)
+    o = run_extend(inp, MONO, workspace=ws)
+    assert_bitwise(o, o_ref, "bf16 D=192 with workspace vs without")
+    assert int(torch.count_nonzero(ws)) == 0
