@@ -251,7 +251,7 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
     // workgroup slot per chunk; the launch's tile slots grow to that.
     const int32_t group = num_heads_q / num_heads_kv;
     const int32_t tset = group > 1 ? group : 1;
-    tiles = std::max(tiles, (cmax + tset - 1) / tset);
+    tiles = std::max(tiles, (cmax + tset - 1) / tset);  // enough for runs of any length
   }
   if ((int64_t)batch * num_heads_q * tiles * (split ? cmax : 1) > kMaxOffset) return DA_EUNSUPPORTED;
   if (split && partials_bytes < partials_bytes_or_max(total_q, num_heads_q, cmax, head_dim))

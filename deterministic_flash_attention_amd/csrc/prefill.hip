@@ -28,6 +28,7 @@
 #include <type_traits>
 
 #include "contract.hpp"
+
 #include "kernels.hpp"
 
 namespace detattn {
@@ -406,6 +407,11 @@ __device__ __forceinline__ void store_output(const PrefillParams& p, const f32x1
 // partial's stores.
 template <int D, bool FP8, bool MONO_PAGED>
 constexpr bool kSpread = MONO_PAGED && (FP8 || D <= 128);
+// Chunks per spread workgroup: a run of four 512-key chunks keeps a spread
+// workgroup's setup small against its 32 blocks while a 32768-token row still
+// finishes in a sixteenth of its single-tile time (runs of 1, 2 and 8 measured
+// the same on the mixed batch).
+constexpr int kSpreadRun = 4;
 
 template <int D, bool FP8, int NW, int WPE, bool SPLIT, bool PAGED, bool WIN>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
@@ -539,10 +545,11 @@ void prefill_kernel(const PrefillParams p) {
   // Chunk spread.  A single-token sequence (a decode row; the query heads of
   // its group packed in one tile) scans its whole context on one wave, a chain
   // that outlasts the rest of a mixed batch.  With a workspace, its chunks
-  // [ds_first, ds_first + ds_chunks) are dealt to the first ds_count =
-  // ds_chunks slots of its tile set, one chunk each, from the empty state as
-  // always (the host sizes the launch's tile slots so that every set has a
-  // slot per chunk); every chunk's partial goes to the workspace, and the slot that
+  // [ds_first, ds_first + ds_chunks) are dealt to the first ds_count slots of
+  // its tile set in contiguous runs of about kSpreadRun chunks, each chunk
+  // from the empty state as always (the host sizes the launch's tile slots so
+  // that every set has enough); every chunk's partial goes to the workspace,
+  // and the slot that
   // completes the set's counter folds them in ascending order and finalises
   // the rows.  That is the fold the single tile runs in registers, on the same
   // partials, so the rows keep their bits.  Sets whose chunks would pass the
@@ -554,15 +561,16 @@ void prefill_kernel(const PrefillParams p) {
     if (ds_try) {
       const int cf = blk_first / kBlocksPerChunk;
       const int cl = nblk > blk_first ? (nblk + kBlocksPerChunk - 1) / kBlocksPerChunk : cf;
-      const int cnt = cl - cf;
-      if (cnt > 1 && cnt <= tset * p.tiles && cl <= p.cmax) {
+      const int cn = cl - cf;
+      const int cnt = min(tset * p.tiles, (cn + kSpreadRun - 1) / kSpreadRun);
+      if (cnt > 1 && cl <= p.cmax) {
         if (ds_slot >= cnt) return;
         dsplit = true;
         ds_first = cf;
-        ds_chunks = cnt;
+        ds_chunks = cn;
         ds_count = cnt;
-        blk_begin = max(blk_first, (cf + ds_slot) * kBlocksPerChunk);
-        blk_end = min(nblk, (cf + ds_slot + 1) * kBlocksPerChunk);
+        blk_begin = max(blk_first, (cf + ds_slot * cn / cnt) * kBlocksPerChunk);
+        blk_end = min(nblk, (cf + (ds_slot + 1) * cn / cnt) * kBlocksPerChunk);
       } else if (ds_slot != 0) {
         return;
       }
@@ -877,11 +885,10 @@ void prefill_kernel(const PrefillParams p) {
     }
   };
 
-  // The end of a chunk inside the block loop folds its partial into the
-  // running total; the end of the loop (chunk c) does the same, or, when the
-  // chunk spread deals this tile set's chunks out, stores the partial in the
-  // workspace (the wave's rows and output tiles; one lane per row for (m, l)).
-  // The accumulator restarts from +0 either way.
+  // The end of a chunk folds its partial into the running total, or, when
+  // the chunk spread deals this tile set's chunks out (SP), stores the partial
+  // in the workspace (the wave's rows and output tiles; one lane per row for
+  // (m, l)).  The accumulator restarts from +0 either way.
   auto fold_chunk = [&]() {
     float ca, cb;
     bool keep;
@@ -896,38 +903,37 @@ void prefill_kernel(const PrefillParams p) {
     m = -INFINITY;
     l = 0.0f;
   };
-  auto end_chunk = [&](int c) {
-    if (kSpread<D, FP8, PAGED && !SPLIT> && dsplit) {
-      const int64_t slot = ((int64_t)c * p.batch + b) * p.hq + head;
-      const rsrc_t mlr = make_rsrc(p.ws_ml + 2 * slot, (uint32_t)nrows * 8u);
-      buf_store8(mlr, (h || dt0) ? kParked : (uint32_t)qrow * 8u, u32x2{f32_bits(m), f32_bits(l)});
-      const rsrc_t ar = make_rsrc(p.ws_acc + slot * D, (uint32_t)nrows * D * 4u);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d = 32 * (dt0 + t) + 8 * q4 + 4 * h;
-          buf_store16(ar, (uint32_t)(qrow * D + d) * 4u,
-                      u32x4{f32_bits(acc[t][4 * q4 + 0]), f32_bits(acc[t][4 * q4 + 1]),
-                            f32_bits(acc[t][4 * q4 + 2]), f32_bits(acc[t][4 * q4 + 3])});
-        }
-    } else {
-      float ca, cb;
-      bool keep;
-      merge_stats(M, L, m, l, ca, cb, keep);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) A[t][i] = merge_elem(A[t][i], acc[t][i], keep, ca, cb);
-    }
+  auto store_chunk = [&](int c) {
+    const int64_t slot = ((int64_t)c * p.batch + b) * p.hq + head;
+    const rsrc_t mlr = make_rsrc(p.ws_ml + 2 * slot, (uint32_t)nrows * 8u);
+    buf_store8(mlr, (h || dt0) ? kParked : (uint32_t)qrow * 8u, u32x2{f32_bits(m), f32_bits(l)});
+    const rsrc_t ar = make_rsrc(p.ws_acc + slot * D, (uint32_t)nrows * D * 4u);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[t][i] = 0.0f;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * (dt0 + t) + 8 * q4 + 4 * h;
+        buf_store16(ar, (uint32_t)(qrow * D + d) * 4u,
+                    u32x4{f32_bits(acc[t][4 * q4 + 0]), f32_bits(acc[t][4 * q4 + 1]),
+                          f32_bits(acc[t][4 * q4 + 2]), f32_bits(acc[t][4 * q4 + 3])});
+        for (int i = 0; i < 4; ++i) acc[t][4 * q4 + i] = 0.0f;
+      }
     m = -INFINITY;
     l = 0.0f;
   };
 
+  // The block loop, instantiated twice where the chunk spread exists: the
+  // copy that stores chunk partials (SP) runs only on spread tiles, so the
+  // registers of the ordinary copy are those of a kernel without the spread.
+  auto run_blocks = [&](auto sp_tag) {
+  constexpr bool SP = decltype(sp_tag)::value;
+  auto end_chunk = [&](int cidx) {
+    if constexpr (SP) {
+      store_chunk(cidx);
+    } else {
+      fold_chunk();
+    }
+  };
   if (blk_begin < blk_end) {
     const int64_t q_head = (int64_t)q_start * p.hq + head;
     const int64_t kv_head = (int64_t)k_start * p.hkv + g;
@@ -1038,7 +1044,7 @@ void prefill_kernel(const PrefillParams p) {
         }
       }
       if constexpr (!SPLIT) {
-        if (j > 0 && blk % kBlocksPerChunk == 0) fold_chunk();
+        if (j > 0 && blk % kBlocksPerChunk == 0) end_chunk(blk / kBlocksPerChunk - 1);
       }
       __syncthreads();
       __builtin_amdgcn_s_setprio(0);
@@ -1125,7 +1131,7 @@ void prefill_kernel(const PrefillParams p) {
         pv_accumulate<D, NT>(acc, dt0, alpha, pb, sV + cur * C::kVStage, lane);
       }
       if constexpr (!SPLIT) {
-        if ((blk + 1) % kBlocksPerChunk == 0 && more) fold_chunk();
+        if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) end_chunk(blk / kBlocksPerChunk);
       }
       if (more) {
         if constexpr (C::kDirect) {
@@ -1138,8 +1144,17 @@ void prefill_kernel(const PrefillParams p) {
       }
       __syncthreads();
     }
-    if constexpr (!SPLIT) end_chunk((blk_end - 1) / kBlocksPerChunk);
       }
+  }
+  };
+  if constexpr (kSpread<D, FP8, PAGED && !SPLIT>) {
+    if (dsplit) {
+      run_blocks(std::true_type{});
+    } else {
+      run_blocks(std::false_type{});
+    }
+  } else {
+    run_blocks(std::false_type{});
   }
 
   if constexpr (kSpread<D, FP8, PAGED && !SPLIT>) {
