@@ -33,6 +33,10 @@ bool check_descales(int32_t dtype, float qd, float kd, float vd) {
   return finite_pos(qd) && finite_pos(kd) && finite_pos(vd);
 }
 
+// Completion counters at the start of a workspace: a fixed region, so that
+// calls of any shape find theirs where every earlier call left zeros.
+constexpr size_t kCounterBytes = (size_t)DA_WORKSPACE_COUNTERS * 4u;
+
 size_t partials_bytes_or_max(int64_t rows, int64_t hq, int64_t chunks, int64_t d) {
   if (rows < 0 || hq < 0 || chunks < 0 || d < 0) return 0;
   const long double n = (long double)rows * hq * chunks * (d + 2) * 4.0L;
@@ -127,11 +131,12 @@ size_t attn_partials_bytes(int64_t rows, int32_t num_heads_q, int32_t max_chunks
 
 size_t attn_extend_workspace_bytes(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
                                    int32_t max_chunks, int32_t head_dim) {
-  if (batch < 0 || num_heads_kv < 0) return 0;
+  if (batch < 0 || num_heads_kv < 0 || num_heads_q < 0 || max_chunks < 0 || head_dim < 0) return 0;
   const size_t cells = partials_bytes_or_max(batch, num_heads_q, max_chunks, head_dim);
   if (cells == std::numeric_limits<size_t>::max()) return cells;
-  // The counters: one int32 per (sequence, kv head), after the partials.
-  return cells + (size_t)batch * (size_t)num_heads_kv * 4u;
+  // The counter region (one int32 per sequence and kv head) first, at a fixed
+  // size, then the partials.
+  return kCounterBytes + cells;
 }
 
 da_status attn_prefill_fwd(int32_t dtype, const void* q, const void* k, const void* v,
@@ -256,6 +261,8 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
   if ((int64_t)batch * num_heads_q * tiles * (split ? cmax : 1) > kMaxOffset) return DA_EUNSUPPORTED;
   if (split && partials_bytes < partials_bytes_or_max(total_q, num_heads_q, cmax, head_dim))
     return DA_EWORKSPACE;
+  if (!split && partials && (int64_t)batch * num_heads_kv > DA_WORKSPACE_COUNTERS)
+    return DA_EUNSUPPORTED;
   if (!split && partials &&
       partials_bytes < attn_extend_workspace_bytes(batch, num_heads_q, num_heads_kv, cmax, head_dim))
     return DA_EWORKSPACE;
@@ -294,9 +301,9 @@ da_status attn_paged_extend_fwd(int32_t dtype, const void* q, const int32_t* cu_
     // Monolithic with a workspace: chunk partials of spread single-token
     // sequences, then their counters.
     const size_t cells = (size_t)cmax * batch * num_heads_q;
-    p.ws_acc = partials;
-    p.ws_ml = partials + cells * head_dim;
-    p.ws_cnt = reinterpret_cast<int32_t*>(partials + cells * (head_dim + 2));
+    p.ws_cnt = reinterpret_cast<int32_t*>(partials);
+    p.ws_acc = partials + kCounterBytes / 4;
+    p.ws_ml = p.ws_acc + cells * head_dim;
     p.part_acc = nullptr;
     p.part_ml = nullptr;
   }

@@ -86,12 +86,19 @@ int32_t attn_num_chunks(int32_t max_seqlen_k);
 size_t attn_partials_bytes(int64_t rows, int32_t num_heads_q, int32_t max_chunks,
                            int32_t head_dim);
 
+/* Completion counters at the start of the monolithic paged extend's
+ * workspace: DA_WORKSPACE_COUNTERS int32 words, 256 KiB, which must be zero
+ * before the first call; every call leaves them zero, so one zero-filled
+ * workspace can serve calls of any shape. */
+#define DA_WORKSPACE_COUNTERS 65536
+
 /* Bytes of the workspace that lets a monolithic attn_paged_extend_fwd spread
- * single-token sequences over workgroups: fp32 chunk partials
+ * single-token sequences over workgroups: the counter region (one counter per
+ * sequence and kv head, batch * num_heads_kv <= DA_WORKSPACE_COUNTERS), then
+ * fp32 chunk partials
  *   acc [max_chunks][batch][num_heads_q][head_dim], then
- *   ml  [max_chunks][batch][num_heads_q][2],
- * then int32 counters [batch][num_heads_kv].  Returns 0 for negative
- * arguments and SIZE_MAX on overflow. */
+ *   ml  [max_chunks][batch][num_heads_q][2].
+ * Returns 0 for negative arguments and SIZE_MAX on overflow. */
 size_t attn_extend_workspace_bytes(int32_t batch, int32_t num_heads_q, int32_t num_heads_kv,
                                    int32_t max_chunks, int32_t head_dim);
 
@@ -180,16 +187,17 @@ da_status attn_decode_split_fwd(int32_t dtype, const void* q, const void* k_cach
  *   partials  DA_SPLIT: the chunk partials, as for attn_prefill_fwd.
  *             DA_MONOLITHIC: NULL, or a workspace of at least
  *             attn_extend_workspace_bytes(batch, Hq, Hkv, max_chunks, head_dim)
- *             bytes (DA_EWORKSPACE if smaller), 16-byte aligned.  With it, a
+ *             bytes (DA_EWORKSPACE if smaller; DA_EUNSUPPORTED if
+ *             batch * Hkv > DA_WORKSPACE_COUNTERS), 16-byte aligned.  With it, a
  *             single-token sequence whose context spans several chunks has its
  *             chunks dealt out to workgroups of the same launch that would
  *             otherwise be idle (the other query heads of its group times the
  *             launch's tile slots); each stores its chunks' partials there, and
  *             the last to finish (a device-scope counter per sequence and kv
  *             head) folds them and writes the rows.  Still one launch, and the
- *             same bits as without the workspace.  Its counters must be zero
- *             before the first call (e.g. the buffer zero-filled once); every
- *             call leaves them zero.  Two calls in flight at once must not
+ *             same bits as without the workspace.  Its counter region must be
+ *             zero before the first call (e.g. the buffer zero-filled once);
+ *             every call leaves it zero.  Two calls in flight at once must not
  *             share a workspace.
  * Each row is bitwise equal to the same row computed by attn_prefill_fwd over
  * the gathered keys, and a decode row to attn_decode_split_fwd's, whichever

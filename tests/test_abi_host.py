@@ -56,7 +56,7 @@ def test_small_helpers(lib):
     assert lib.attn_partials_bytes(8192, 32, 16, 128) == 8192 * 32 * 16 * 130 * 4
     assert lib.attn_partials_bytes(-1, 32, 16, 128) == 0
     lib.attn_extend_workspace_bytes.restype = ctypes.c_size_t
-    assert lib.attn_extend_workspace_bytes(11, 32, 8, 64, 128) == 11 * 32 * 64 * 130 * 4 + 11 * 8 * 4
+    assert lib.attn_extend_workspace_bytes(11, 32, 8, 64, 128) == (1 << 18) + 11 * 32 * 64 * 130 * 4
     assert lib.attn_extend_workspace_bytes(-1, 32, 8, 64, 128) == 0
     for s in range(5):
         assert lib.attn_status_str(s).decode().startswith("DA_")
@@ -194,6 +194,7 @@ def _extend_args(**over):
     (dict(schedule=1, part=FAKE, part_bytes=4096), DA_EWORKSPACE),
     (dict(part=FAKE, part_bytes=4096), DA_EWORKSPACE),   # monolithic, workspace too small
     (dict(part=FAKE + 4, part_bytes=1 << 30), DA_EINVAL),  # monolithic, misaligned workspace
+    (dict(part=FAKE, part_bytes=1 << 40, batch=70000, hkv=1, hq=1), DA_EUNSUPPORTED),  # > 65536 counters
     (dict(max_q=1 << 28), DA_EUNSUPPORTED),   # beyond 32-bit descriptor offsets
     (dict(wl=-7), DA_EINVAL),
     (dict(batch=0), DA_OK),                   # no work: nothing launched

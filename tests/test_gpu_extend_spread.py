@@ -21,13 +21,17 @@ QL = [300, 1, 37, 1, 700, 1, 777, 1, 1]
 LONG = 1  # the 5000-token decode row: 10 chunks
 
 
+COUNTER_WORDS = 65536  # the counter region that opens the workspace
+
+
 def _regions(ws, inp):
-    """(ml [cmax, batch, hq, 2], counters [batch, hkv]) views of the workspace."""
+    """(ml [cmax, batch, hq, 2], counter region) views of the workspace."""
     import deterministic_flash_attention_amd as dfa
     b, cmax = len(inp.q_lens), dfa.attn_num_chunks(max(inp.ctx_lens))
     cells = cmax * b * inp.hq
-    ml = ws[cells * inp.d:cells * (inp.d + 2)].view(cmax, b, inp.hq, 2)
-    cnt = ws[cells * (inp.d + 2):].view(torch.int32)[:b * inp.hkv]
+    part = ws[COUNTER_WORDS:]
+    ml = part[cells * inp.d:cells * (inp.d + 2)].view(cmax, b, inp.hq, 2)
+    cnt = ws[:COUNTER_WORDS].view(torch.int32)
     return ml, cnt
 
 
@@ -90,3 +94,23 @@ def test_no_spread_for_bf16_d192():
     o = run_extend(inp, MONO, workspace=ws)
     assert_bitwise(o, o_ref, "bf16 D=192 with workspace vs without")
     assert int(torch.count_nonzero(ws)) == 0
+
+
+def test_workspace_reused_across_batches():
+    """One zero-filled workspace, sized for the largest call, serves launches of
+    different batch shapes in turn (each call's partials land where another
+    call's counters would be if the counters moved with the shape)."""
+    import deterministic_flash_attention_amd as dfa
+    batches = [(CTX, QL, 8, 2), ([9000, 1, 700], [1, 1, 700], 8, 2), (CTX[:4], QL[:4], 8, 4)]
+    inps = [synth.extend_inputs(71 + i, c, q, hq, hkv, 128) for i, (c, q, hq, hkv) in
+            enumerate(batches)]
+    nbytes = max(dfa.attn_extend_workspace_bytes(len(i.q_lens), i.hq, i.hkv,
+                                                 dfa.attn_num_chunks(max(i.ctx_lens)), i.d)
+                 for i in inps)
+    ws = torch.zeros((nbytes + 3) // 4, dtype=torch.float32, device="cuda")
+    for rnd in range(2):
+        for i, inp in enumerate(inps):
+            o_ref = run_extend(inp, MONO)
+            o = run_extend(inp, MONO, workspace=ws)
+            assert_bitwise(o, o_ref, f"batch {i} round {rnd} with a shared workspace")
+            assert int(torch.count_nonzero(ws[:COUNTER_WORDS])) == 0
