@@ -213,6 +213,7 @@ struct DirectStager {
     for (int u = 0; u < kVPer; ++u) voff[u] = slot_offset(wave + u * NW, lane, kVSlots, rb);
   }
   __device__ __forceinline__ void prefetch(int, int) {}  // nothing to look up
+  __device__ __forceinline__ void latch() {}
   // Byte offset of block blk's first row from the descriptors' base row kbase.
   // It is negative (wrapping to a huge unsigned value) for the block holding
   // kbase when kbase is not block-aligned: rows below kbase then fail the range
@@ -274,7 +275,9 @@ struct PagedDirectStager {
   int max_pages;
   int page;                 // this wave's page of every block (0..3)
   int sub;                  // and its rank among the waves of that page
-  int32_t kent, vent;       // table entries of this wave's pages of the next K and V blocks
+  int32_t kent, vent;       // table entries of this wave's pages of the next K and V blocks,
+                            // as loaded
+  int32_t kpg, vpg;         // the same, scalar, for the issue that uses them
 
   static __device__ __forceinline__ uint32_t slot_offset(int sp, int lane, int slots,
                                                          uint32_t token_bytes) {
@@ -303,11 +306,18 @@ struct PagedDirectStager {
   // Read this wave's table entries of K block kblk and V block vblk, to be
   // issued next; indices are clamped into the table row (entries of pages
   // without a live token are never used).
+  // The entries stay in vector registers until latch(), at the start of the
+  // staging event that uses them, before that event issues any load:
+  // converting them right after the loads would wait for every load issued
+  // before them, the block's K/V loads included.
   __device__ __forceinline__ void prefetch(int kblk, int vblk) {
-    // One entry per wave (its page): read into scalar registers, so the page
-    // descriptors stay scalar too.
-    kent = uniform(table[max(0, min(kblk * 4 + page, max_pages - 1))]);
-    vent = uniform(table[max(0, min(vblk * 4 + page, max_pages - 1))]);
+    kent = table[max(0, min(kblk * 4 + page, max_pages - 1))];
+    vent = table[max(0, min(vblk * 4 + page, max_pages - 1))];
+  }
+  // One entry per wave (its page): scalar, so the page descriptors are too.
+  __device__ __forceinline__ void latch() {
+    kpg = uniform(kent);
+    vpg = uniform(vent);
   }
   // Descriptor of this wave's page of block blk, whose table entry is pg.
   __device__ __forceinline__ rsrc_t page_rsrc(const unsigned char* cache, int blk,
@@ -319,7 +329,7 @@ struct PagedDirectStager {
   }
   // Issue K block blk / V block blk: the last prefetch must have named it.
   __device__ __forceinline__ void issue_k(int blk, unsigned char* ks, int) const {
-    const rsrc_t r = page_rsrc(kc, blk, kent);
+    const rsrc_t r = page_rsrc(kc, blk, kpg);
     unsigned char* const base = ks + page * KPAGE;
 #pragma unroll
     for (int u = 0; u < kKPer; ++u) {
@@ -328,7 +338,7 @@ struct PagedDirectStager {
     }
   }
   __device__ __forceinline__ void issue_v(int blk, unsigned char* vs, int) const {
-    const rsrc_t r = page_rsrc(vc, blk, vent);
+    const rsrc_t r = page_rsrc(vc, blk, vpg);
     unsigned char* const base = vs + page * (16 * G::kVRow);
 #pragma unroll
     for (int u = 0; u < kVPer; ++u) {
@@ -1009,6 +1019,7 @@ void prefill_kernel(const PrefillParams p) {
     // up (paged caches) the blocks of event e+1.
     dst.prefetch(blk_begin, blk_begin - 1);
     auto event = [&](int e) {
+      dst.latch();
       if (e + 1 < n) dst.issue_k(blk_begin + e + 1, sK + ((e + 1) & 1) * C::kKStage, wv);
       if (e >= 0 && e < n) dst.issue_v(blk_begin + e, sV + (e & 1) * C::kVStage, wv);
       dst.prefetch(blk_begin + e + 2, blk_begin + e + 1);
@@ -1078,6 +1089,7 @@ void prefill_kernel(const PrefillParams p) {
     auto dst = make_direct();
     if constexpr (C::kDirect) {
       dst.prefetch(blk_begin, blk_begin);
+      dst.latch();
       dst.issue_k(blk_begin, sK, wv);
       dst.issue_v(blk_begin, sV, wv);
     } else {
@@ -1111,6 +1123,7 @@ void prefill_kernel(const PrefillParams p) {
       if (more) {
         if constexpr (C::kDirect) {
           dst.prefetch(blk + 1, blk + 1);
+          dst.latch();
           dst.issue_k(blk + 1, sK + (cur ^ 1) * C::kKStage, wv);
           dst.issue_v(blk + 1, sV + (cur ^ 1) * C::kVStage, wv);
         } else {
