@@ -48,6 +48,27 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, unsigned char* lds_seg,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
       r, (__attribute__((address_space(3))) void*)lds_seg, 16, off, 0, 0, 0);
 }
+// The words of make_rsrc(base, num_records), for the assembly form below.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, num_records, 0x00020000u};
+}
+// buf_load16_lds issued from inline assembly.  The compiler does not count
+// this load among its outstanding vector-memory operations, so it places no
+// wait for it before later LDS reads (which may be of other stages, with the
+// load meant to stay in flight); the caller waits for it with wait_vm_n or
+// wait_vm before the barrier that publishes its data.  lds_seg must be
+// wave-uniform; M0 takes it, with the one wait state an LDS-destination load
+// needs after M0 is written.
+__device__ __forceinline__ void buf_load16_lds_async(u32x4 rw, unsigned char* lds_seg,
+                                                     uint32_t off) {
+  const uint32_t m = uniform((uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) unsigned char*)lds_seg));
+  const u32x4 w = {uniform(rw[0]), uniform(rw[1]), uniform(rw[2]), uniform(rw[3])};
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(m), "v"(off), "s"(w)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Workgroup barrier that completes this wave's LDS operations (so its LDS
 // writes are visible to every wave after it) but not its vector-memory loads:

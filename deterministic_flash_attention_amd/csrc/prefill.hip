@@ -327,23 +327,67 @@ struct PagedDirectStager {
     return make_rsrc(cache + (ok ? (int64_t)pg * page_bytes : 0),
                      ok ? (uint32_t)(live - 1) * token_bytes + (uint32_t)G::kRowBytes : 0u);
   }
-  // Issue K block blk / V block blk: the last prefetch must have named it.
+  // The same descriptor as words, for buf_load16_lds_async.
+  __device__ __forceinline__ u32x4 page_words(const unsigned char* cache, int blk,
+                                              int32_t pg) const {
+    const int live = min(16, lk - (blk * kBlockKeys + 16 * page));
+    const bool ok = live > 0 && pg >= 0 && (int64_t)pg < num_pages;
+    return rsrc_words(cache + (ok ? (int64_t)pg * page_bytes : 0),
+                      ok ? (uint32_t)(live - 1) * token_bytes + (uint32_t)G::kRowBytes : 0u);
+  }
+  // Table entries of this wave's page of blocks [blk0, blk0 + 64), lane i
+  // holding block blk0 + i's (clamped into the table row like prefetch).
+  __device__ __forceinline__ int32_t entries(int blk0, int lane) const {
+    return table[max(0, min((blk0 + lane) * 4 + page, max_pages - 1))];
+  }
+  // A scalar table entry for the next issue_k / issue_v.
+  __device__ __forceinline__ void use_entry(int32_t pg) { kpg = vpg = pg; }
+  // Loads one issue_k + issue_v makes for a wave of rank sb in its page.
+  static constexpr int loads_per_block(int sb) {
+    int n = 0;
+    for (int u = 0; u < kKPer; ++u) n += (kKPer * kWavesPerPage == kKSegs || sb + u * kWavesPerPage < kKSegs);
+    for (int u = 0; u < kVPer; ++u) n += (kVPer * kWavesPerPage == kVSegs || sb + u * kWavesPerPage < kVSegs);
+    return n;
+  }
+  // Issue K block blk / V block blk: the last prefetch (or use_entry) must
+  // have named it.  ASYNC issues the loads from inline assembly (they stay in
+  // flight past later LDS reads; the caller waits for them).
+  template <bool ASYNC = false>
   __device__ __forceinline__ void issue_k(int blk, unsigned char* ks, int) const {
-    const rsrc_t r = page_rsrc(kc, blk, kpg);
     unsigned char* const base = ks + page * KPAGE;
+    if constexpr (ASYNC) {
+      const u32x4 rw = page_words(kc, blk, kpg);
 #pragma unroll
-    for (int u = 0; u < kKPer; ++u) {
-      const int sp = sub + u * kWavesPerPage;
-      if (kKPer * kWavesPerPage == kKSegs || sp < kKSegs) buf_load16_lds(r, base + sp * 1024, koff[u]);
+      for (int u = 0; u < kKPer; ++u) {
+        const int sp = sub + u * kWavesPerPage;
+        if (kKPer * kWavesPerPage == kKSegs || sp < kKSegs) buf_load16_lds_async(rw, base + sp * 1024, koff[u]);
+      }
+    } else {
+      const rsrc_t r = page_rsrc(kc, blk, kpg);
+#pragma unroll
+      for (int u = 0; u < kKPer; ++u) {
+        const int sp = sub + u * kWavesPerPage;
+        if (kKPer * kWavesPerPage == kKSegs || sp < kKSegs) buf_load16_lds(r, base + sp * 1024, koff[u]);
+      }
     }
   }
+  template <bool ASYNC = false>
   __device__ __forceinline__ void issue_v(int blk, unsigned char* vs, int) const {
-    const rsrc_t r = page_rsrc(vc, blk, vpg);
     unsigned char* const base = vs + page * (16 * G::kVRow);
+    if constexpr (ASYNC) {
+      const u32x4 rw = page_words(vc, blk, vpg);
 #pragma unroll
-    for (int u = 0; u < kVPer; ++u) {
-      const int sp = sub + u * kWavesPerPage;
-      if (kVPer * kWavesPerPage == kVSegs || sp < kVSegs) buf_load16_lds(r, base + sp * 1024, voff[u]);
+      for (int u = 0; u < kVPer; ++u) {
+        const int sp = sub + u * kWavesPerPage;
+        if (kVPer * kWavesPerPage == kVSegs || sp < kVSegs) buf_load16_lds_async(rw, base + sp * 1024, voff[u]);
+      }
+    } else {
+      const rsrc_t r = page_rsrc(vc, blk, vpg);
+#pragma unroll
+      for (int u = 0; u < kVPer; ++u) {
+        const int sp = sub + u * kWavesPerPage;
+        if (kVPer * kWavesPerPage == kVSegs || sp < kVSegs) buf_load16_lds(r, base + sp * 1024, voff[u]);
+      }
     }
   }
 };
@@ -543,8 +587,6 @@ void prefill_kernel(const PrefillParams p) {
   const int last = min(r0 + C::kTileRows, nrows) - 1;
   const int kstart = row_lo(pos(r0));    // first key visible to some row
   const int kend = row_hi(pos(last));    // past the last key visible to some row
-  const int klo_full = row_lo(pos(last));  // keys in [klo_full, kfull) are visible to every row
-  const int kfull = row_hi(pos(r0));
   const int nblk = kend > kstart ? (kend + kBlockKeys - 1) / kBlockKeys : 0;
   const int blk_first = kend > kstart ? kstart / kBlockKeys : 0;
   int blk_begin = blk_first, blk_end = nblk;
@@ -604,6 +646,13 @@ void prefill_kernel(const PrefillParams p) {
   const int wlo = wactive ? row_lo(pos(wrow0)) : 0;
   const int wlo_max = wactive ? row_lo(pos(wrow_last)) : 0;  // a lower edge masks blocks below it
   const int whi = wactive ? row_hi(pos(wrow_last)) : 0;
+  const int whi_min = wactive ? row_hi(pos(wrow0)) : 0;  // an upper edge masks blocks past it
+  // Bounds of the unmasked class: this wave's for sliding windows and paged
+  // caches; the tile's (every row of the tile sees the block) for contiguous
+  // causal tiles, where the per-wave class measured slower.  A fully visible
+  // block gives the same bits in either class.
+  const int mlo = (WIN || PAGED) ? wlo_max : row_lo(pos(last));
+  const int mhi = (WIN || PAGED) ? whi_min : row_hi(pos(r0));
   const int wblk_first = wlo / kBlockKeys;
   const int wblk_end = whi > wlo ? (whi + kBlockKeys - 1) / kBlockKeys : 0;
   auto wave_live = [&](int blk) { return blk >= wblk_first && blk < wblk_end; };
@@ -669,7 +718,7 @@ void prefill_kernel(const PrefillParams p) {
         for (int i = 0; i < 16; ++i) acc[t][i] = A[t][i] = 0.0f;
       auto softmax = [&](int blk, const f32x16 (&s)[2], float& alpha, u32x4 (&pb)[4]) {
         const int b0 = kBlockKeys * blk;
-        if (b0 >= klo_full && b0 + kBlockKeys <= kfull) {
+        if (b0 >= mlo && b0 + kBlockKeys <= mhi) {
           softmax_block<kNoMask>(s, h, c, 0, 0, m, l, alpha, pb);
         } else if (b0 >= wlo_max) {
           softmax_block<kMaskHi>(s, h, c, 0, hi - b0, m, l, alpha, pb);
@@ -882,11 +931,13 @@ void prefill_kernel(const PrefillParams p) {
       acc[j][i] = 0.0f;
       A[j][i] = 0.0f;
     }
-  // Softmax update of block blk, masked according to its class for this tile
-  // and wave.
+  // Softmax update of block blk, masked according to its class: no mask where
+  // every row (of the wave, or of the tile) sees all 64 keys, the upper edge
+  // alone where no row of the wave has its lower edge inside the block, both
+  // edges otherwise (the three give the same bits wherever a key is visible).
   auto softmax = [&](int blk, const f32x16 (&s)[2], float& alpha, u32x4 (&pb)[4]) {
     const int b0 = kBlockKeys * blk;
-    if (b0 >= klo_full && b0 + kBlockKeys <= kfull) {
+    if (b0 >= mlo && b0 + kBlockKeys <= mhi) {
       softmax_block<kNoMask>(s, h, c, 0, 0, m, l, alpha, pb);
     } else if (b0 >= wlo_max) {
       softmax_block<kMaskHi>(s, h, c, 0, hi - b0, m, l, alpha, pb);
@@ -971,28 +1022,124 @@ void prefill_kernel(const PrefillParams p) {
     };
     const int wv = uniform(wave);
     // The direct stager of this sequence's keys (packed rows or cache pages).
-    auto make_direct = [&]() {
+    auto make_direct = [&](int ln) {
       if constexpr (C::kDirectK) {
         DirectStager<D, NW, true> st;  // K only
-        st.init(wv, lane, kr, vr, kv_row_bytes, kstart);
+        st.init(wv, ln, kr, vr, kv_row_bytes, kstart);
         return st;
       } else if constexpr (!C::kDirect) {
         return 0;  // staged through registers
       } else if constexpr (PAGED) {
         PagedDirectStager<D, NW, C::kKPage> st;
         const int64_t head_off = (int64_t)g * p.head_stride * G::kEs;
-        st.init(wv, lane, static_cast<const unsigned char*>(p.k) + head_off,
+        st.init(wv, ln, static_cast<const unsigned char*>(p.k) + head_off,
                 static_cast<const unsigned char*>(p.v) + head_off, table, p.num_pages,
                 p.page_stride * G::kEs, (uint32_t)(p.token_stride * G::kEs), lk, p.max_pages);
         return st;
       } else {
         DirectStager<D, NW> st;
-        st.init(wv, lane, kr, vr, kv_row_bytes, kstart);
+        st.init(wv, ln, kr, vr, kv_row_bytes, kstart);
         return st;
       }
     };
 
     if constexpr (C::kDirect && NW == 8) {
+    if constexpr (SP) {
+    // Spread tiles of a single-token sequence (bf16 paged caches).  Only the
+    // waves holding the tile's rows compute (one wave for a kv group of up to
+    // 32 query heads), every wave stages, and with no second wave of the SIMD
+    // to share the work there is nothing to ping-pong: a block's loads have
+    // only one wave's block of arithmetic to hide under.  So the blocks go
+    // through three K/V stages, the third at the end of the Q tile's region
+    // (whose start keeps the Q rows of up to kDeepRows rows; the waves read
+    // their Q^T operands from LDS, which keeps their registers at what the
+    // ping-pong needs), and step j issues the loads of block j+2 from inline
+    // assembly, so they stay in flight while the step computes block j; the
+    // step ends by waiting for block j+1's loads (this wave's loads of block
+    // j+2 may stay outstanding) and a barrier that leaves them in flight.
+    // Block b lives in stage b % 3 (blocks relative to blk_begin) and is
+    // written in step b - 2, after the barrier that ended step b - 3, the last
+    // reads of that stage.  A tile with more rows uses two stages, one block
+    // ahead.  The page-table entries of the run arrive in one vector load at
+    // the start and reach the loads by readlane, so no table load sits behind
+    // staging loads in the in-order wait.  Each block's arithmetic is the one
+    // every schedule runs (scores, softmax update, rescale, P V), so the bits
+    // are the same.
+    constexpr int kSt2 = C::kQBytes - C::kKStage - C::kVStage;  // third stage, K then V
+    constexpr int kDeepRows = kSt2 / G::kQRow / 32 * 32;
+    static_assert(kDeepRows >= 32, "the third stage leaves room for one wave's Q rows");
+    const int n = blk_end - blk_begin;
+    const bool deep = nrows <= kDeepRows;
+    const int ns = deep ? 3 : 2;  // stages, and blocks in flight plus one
+    int lane_x = lane;
+    asm volatile("" : "+v"(lane_x));
+    auto dst = make_direct(lane_x);
+    using St = decltype(dst);
+    static_assert(St::kWavesPerPage == 2, "two waves per page region");
+    constexpr int kL0 = St::loads_per_block(0), kL1 = St::loads_per_block(1);
+    auto kst = [&](int sidx) { return sidx == 2 ? sQ + kSt2 : sK + sidx * C::kKStage; };
+    auto vst = [&](int sidx) { return sidx == 2 ? sQ + kSt2 + C::kKStage : sV + sidx * C::kVStage; };
+    int ebase = blk_begin;
+    int32_t ent = dst.entries(ebase, lane);
+    // Scalar table entry of block blk (blocks in increasing order); a run past
+    // 64 blocks reloads the entries, waiting for them at once, so that no wait
+    // for them remains on the path of the steps that follow.
+    auto entry = [&](int blk) {
+      if (blk - ebase >= kWave) {
+        ebase = blk;
+        ent = dst.entries(ebase, lane);
+        asm volatile("" ::"v"(ent));
+      }
+      return __builtin_amdgcn_readlane(ent, blk - ebase);
+    };
+    for (int b = 0; b < ns - 1 && b < n; ++b) {
+      dst.use_entry(entry(blk_begin + b));
+      dst.issue_k(blk_begin + b, kst(b), wv);
+      dst.issue_v(blk_begin + b, vst(b), wv);
+    }
+    for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
+      const int r = x / G::kChunks16, col = x % G::kChunks16;
+      if (!deep || r < kDeepRows)
+        lds_store16(sQ, (uint32_t)(r * G::kQRow + col * 16),
+                    buf_load16(qr, (uint32_t)(r0 + r) * q_row_bytes + (uint32_t)col * 16u));
+    }
+    wait_vm();
+    __syncthreads();
+    const unsigned char* const sQw = sQ + (32 * qg) * G::kQRow;
+    int cur = 0;  // stage of block j; block j + ns - 1 goes to the stage before it
+    for (int j = 0; j < n; ++j) {
+      const int blk = blk_begin + j;
+      const int ahead_st = cur == 0 ? ns - 1 : cur - 1;
+      const bool ahead = j + ns - 1 < n;
+      if (ahead) {
+        dst.use_entry(entry(blk + ns - 1));
+        dst.template issue_k<true>(blk + ns - 1, kst(ahead_st), wv);
+        dst.template issue_v<true>(blk + ns - 1, vst(ahead_st), wv);
+      }
+      if (wave_live(blk)) {
+        f32x16 s[2];
+        qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, kst(cur), lane);
+        float alpha;
+        u32x4 pb[4];
+        softmax(blk, s, alpha, pb);
+        pv_accumulate<D, NT>(acc, dt0, alpha, pb, vst(cur), lane);
+      }
+      if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) end_chunk(blk / kBlocksPerChunk);
+      // Block j+1 has landed; with three stages this wave's loads of block
+      // j+2 (issued last) may stay outstanding.
+      if (ahead && deep) {
+        if (dst.sub == 0) {
+          wait_vm_n<kL0>();
+        } else {
+          wait_vm_n<kL1>();
+        }
+      } else {
+        wait_vm();
+      }
+      barrier_lds();
+      cur = cur == ns - 1 ? 0 : cur + 1;
+    }
+    } else {
     // Ping-pong (bf16 staged directly, two waves per SIMD).  Each wave
     // alternates an MFMA phase (P V of block j-1, then S_j = K_j Q^T) and a
     // VALU phase (the softmax update of block j and the rescale of acc), one
@@ -1013,7 +1160,7 @@ void prefill_kernel(const PrefillParams p) {
     // earlier in the same stage and before the first read of its own block.
     const int n = blk_end - blk_begin;
     const int lag = wv >= NW / 2 ? 1 : 0;
-    auto dst = make_direct();
+    auto dst = make_direct(lane);
     // event e: K block e+1 -> K stage (e+1)&1, V block e -> V stage e&1 (relative
     // blocks).  A wave's events run in order, so after issuing event e it looks
     // up (paged caches) the blocks of event e+1.
@@ -1071,6 +1218,7 @@ void prefill_kernel(const PrefillParams p) {
     if (wave_live(blk_end - 1)) pv_mfma<D, NT>(acc, dt0, pb, sV + ((n - 1) & 1) * C::kVStage, lane);
     if constexpr (!SPLIT) end_chunk((blk_end - 1) / kBlocksPerChunk);
     if (!lag) __syncthreads();
+    }
       } else {
     const int n = blk_end - blk_begin;
     KVStager<D, FP8, NW> rst;
@@ -1086,7 +1234,7 @@ void prefill_kernel(const PrefillParams p) {
                  kv_row_bytes, tid);
       }
     };
-    auto dst = make_direct();
+    auto dst = make_direct(lane);
     if constexpr (C::kDirect) {
       dst.prefetch(blk_begin, blk_begin);
       dst.latch();
@@ -1163,15 +1311,6 @@ void prefill_kernel(const PrefillParams p) {
   if constexpr (kSpread<D, FP8, PAGED && !SPLIT>) {
     if (dsplit) {
       run_blocks(std::true_type{});
-    } else {
-      run_blocks(std::false_type{});
-    }
-  } else {
-    run_blocks(std::false_type{});
-  }
-
-  if constexpr (kSpread<D, FP8, PAGED && !SPLIT>) {
-    if (dsplit) {
       // Count this workgroup in (its partial stores made visible at device
       // scope first); the one that completes the set's count folds every chunk
       // partial in ascending order, finalises the rows and clears the counter
@@ -1226,6 +1365,7 @@ void prefill_kernel(const PrefillParams p) {
       return;
     }
   }
+  run_blocks(std::false_type{});
   if constexpr (SPLIT) {
     store_partial<D, NT>(p, acc, m, l, dt0, chunk, q_start, head, nrows, rs, qrow, h);
   } else {
