@@ -556,16 +556,29 @@ void prefill_kernel(const PrefillParams p) {
   // With a workspace, a single-token sequence may spread its chunks over the
   // workgroup slots of its tile set (query heads of the set times the tile
   // slots of the launch); see the chunk spread below.
-  const bool ds_try = kSpread<D, FP8, PAGED && !SPLIT> && lq == 1 && p.ws_cnt != nullptr;
+  // A group larger than one tile (several tiles per set) keeps the tiles.
+  const bool ds_try = kSpread<D, FP8, PAGED && !SPLIT> && lq == 1 && p.ws_cnt != nullptr &&
+                      (pack ? grp_size : 1) <= C::kTileRows;
   const int tset = pack ? grp_size : 1;                // query heads per tile set
-  const int ds_slot = tile_rev * tset + head % tset;   // this workgroup's slot in the set
-  if (!ds_try && pack && head % grp_size != 0) return;
-  head -= head % tset;  // the tile set's first query head
+  const int hsub = head % tset;                        // this workgroup's head in the set
+  const int ds_slot = tile_rev * tset + hsub;          // this workgroup's slot in the set
+  head -= hsub;  // the tile set's first query head
   const int nrows = pack ? grp_size : lq;  // real rows of this tile set
   const int64_t rs = pack ? 1 : p.hq;      // row stride in head rows
   auto pos = [&](int i) { return pack ? 0 : i; };  // query position of local row i
   const int ntiles = (nrows + C::kTileRows - 1) / C::kTileRows;
-  const int tile = ds_try ? 0 : ntiles - 1 - tile_rev;
+  // Tiles of a packed set (a group larger than one tile has several) go to
+  // the workgroups of its heads at the first tile slot: the launch sizes its
+  // tile slots by query rows, one for a single-token sequence.
+  int tile;
+  if (ds_try) {
+    tile = 0;
+  } else if (pack) {
+    if (tile_rev != 0 || hsub >= ntiles) return;
+    tile = ntiles - 1 - hsub;
+  } else {
+    tile = ntiles - 1 - tile_rev;
+  }
   if (tile < 0) return;
   const int r0 = tile * C::kTileRows;
   const int g = head / grp_size;

@@ -89,6 +89,28 @@ def test_extend_equals_prefill_and_decode(dtype, d):
     assert_bitwise(l_dec, l_ext[ext_last.to(l_ext.device)], "decode lse vs extend last row")
 
 
+# Single-token rows of kv groups larger than one tile: a group packs into one
+# tile set of several tiles (256 rows for bf16 up to D = 128, 128 for bf16
+# D = 192 on four waves and for e4m3 D = 192), computed by the workgroups of
+# the set's heads.
+@pytest.mark.parametrize("dtype,d,hq", [("bf16", 128, 512), ("bf16", 192, 256),
+                                        ("fp8", 192, 256)])
+def test_groups_larger_than_a_tile(dtype, d, hq):
+    ctx, ql = [3000, 700, 1, 1500], [1, 5, 1, 1]
+    inp = synth.extend_inputs(47, ctx, ql, hq, 1, d, dtype=dtype)
+    note(f"paged extend {dtype} d={d} group={hq} ctx={ctx} q={ql}")
+    o, lse = run_extend(inp, MONO, return_lse=True)
+    ref, ref_lse = oracle_extend(inp)
+    compare(o, ref, dtype == "fp8", label=f"O group {hq}")
+    _check_lse(lse, ref_lse)
+    o_s, lse_s = run_extend(inp, SPLIT, return_lse=True)
+    assert_bitwise(o_s, o, "O split vs monolithic")
+    assert_bitwise(lse_s, lse, "lse split vs monolithic")
+    o_w, lse_w = run_extend(inp, MONO, return_lse=True, workspace=extend_workspace(inp))
+    assert_bitwise(o_w, o, "O with workspace vs without")
+    assert_bitwise(lse_w, lse, "lse with workspace vs without")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_extend_split_equals_monolithic(dtype):
     inp = synth.extend_inputs(49, MIX_CTX, MIX_Q, 4, 2, 128, dtype=dtype)

@@ -47,9 +47,14 @@ def _spread_vs_single(inp, window=(-1, -1), calls=2):
     return o_ref, ws
 
 
+# bf16 spread tiles run a loop of their own: three K/V stages while the kv
+# group's query heads fit below the third stage (96 rows at D = 128, 64 at
+# D = 64), two beyond; groups of 64 (two computing waves), 128 and, at D = 64,
+# 96 take the other paths.
 @pytest.mark.parametrize("dtype,d,hq,hkv", [("bf16", 128, 8, 2), ("bf16", 64, 4, 1),
                                             ("bf16", 128, 4, 4), ("fp8", 128, 4, 2),
-                                            ("fp8", 192, 4, 4)])
+                                            ("fp8", 192, 4, 4), ("bf16", 128, 64, 1),
+                                            ("bf16", 128, 128, 1), ("bf16", 64, 96, 1)])
 def test_spread_equals_single_tile(dtype, d, hq, hkv):
     inp = synth.extend_inputs(61, CTX, QL, hq, hkv, d, dtype=dtype)
     note(f"chunk spread {dtype} d={d} hq={hq} hkv={hkv} ctx={CTX} q={QL}")
@@ -61,6 +66,18 @@ def test_spread_equals_single_tile(dtype, d, hq, hkv):
     m, l = ml[:nch, LONG, :, 0], ml[:nch, LONG, :, 1]
     assert torch.isfinite(m).all() and (l >= 1.0).all()
     assert int(torch.count_nonzero(ml[nch:, LONG])) == 0
+
+
+@pytest.mark.parametrize("hq", [64, 128])
+def test_spread_large_groups_against_oracle(hq):
+    """Single-token rows of kv groups of 64 and 128 query heads (three and
+    two K/V stages in the spread tile), against the oracle."""
+    inp = synth.extend_inputs(67, CTX, QL, hq, 1, 128)
+    o, _ = _spread_vs_single(inp, calls=1)
+    cq = inp.cu_seqlens_q.tolist()
+    rows = [cq[b] for b, q in enumerate(QL) if q == 1]
+    ref = oracle_extend(inp, rows=rows)[0]
+    compare(o, ref, False, rows=rows, label=f"O single-token rows, group {hq}, chunk spread")
 
 
 def test_spread_against_oracle():
