@@ -1035,23 +1035,23 @@ void prefill_kernel(const PrefillParams p) {
     };
     const int wv = uniform(wave);
     // The direct stager of this sequence's keys (packed rows or cache pages).
-    auto make_direct = [&](int ln) {
+    auto make_direct = [&]() {
       if constexpr (C::kDirectK) {
         DirectStager<D, NW, true> st;  // K only
-        st.init(wv, ln, kr, vr, kv_row_bytes, kstart);
+        st.init(wv, lane, kr, vr, kv_row_bytes, kstart);
         return st;
       } else if constexpr (!C::kDirect) {
         return 0;  // staged through registers
       } else if constexpr (PAGED) {
         PagedDirectStager<D, NW, C::kKPage> st;
         const int64_t head_off = (int64_t)g * p.head_stride * G::kEs;
-        st.init(wv, ln, static_cast<const unsigned char*>(p.k) + head_off,
+        st.init(wv, lane, static_cast<const unsigned char*>(p.k) + head_off,
                 static_cast<const unsigned char*>(p.v) + head_off, table, p.num_pages,
                 p.page_stride * G::kEs, (uint32_t)(p.token_stride * G::kEs), lk, p.max_pages);
         return st;
       } else {
         DirectStager<D, NW> st;
-        st.init(wv, ln, kr, vr, kv_row_bytes, kstart);
+        st.init(wv, lane, kr, vr, kv_row_bytes, kstart);
         return st;
       }
     };
@@ -1060,16 +1060,16 @@ void prefill_kernel(const PrefillParams p) {
     if constexpr (SP) {
     // Spread tiles of a single-token sequence (bf16 paged caches).  Only the
     // waves holding the tile's rows compute (one wave for a kv group of up to
-    // 32 query heads), every wave stages, and with no second wave of the SIMD
-    // to share the work there is nothing to ping-pong: a block's loads have
-    // only one wave's block of arithmetic to hide under.  So the blocks go
+    // 32 query heads), and with no second wave of the SIMD to share the work
+    // there is nothing to ping-pong: a block's loads have only one wave's
+    // block of arithmetic to hide under.  So the blocks go
     // through three K/V stages, the third at the end of the Q tile's region
     // (whose start keeps the Q rows of up to kDeepRows rows; the waves read
     // their Q^T operands from LDS, which keeps their registers at what the
     // ping-pong needs), and step j issues the loads of block j+2 from inline
     // assembly, so they stay in flight while the step computes block j; the
-    // step ends by waiting for block j+1's loads (this wave's loads of block
-    // j+2 may stay outstanding) and a barrier that leaves them in flight.
+    // step ends by waiting for block j+1's loads (a staging wave's loads of
+    // block j+2 may stay outstanding) and a barrier that leaves them in flight.
     // Block b lives in stage b % 3 (blocks relative to blk_begin) and is
     // written in step b - 2, after the barrier that ended step b - 3, the last
     // reads of that stage.  A tile with more rows uses two stages, one block
@@ -1084,12 +1084,28 @@ void prefill_kernel(const PrefillParams p) {
     const int n = blk_end - blk_begin;
     const bool deep = nrows <= kDeepRows;
     const int ns = deep ? 3 : 2;  // stages, and blocks in flight plus one
+    // The second half of the waves stage, one cache page each (a wave that
+    // computes a block while its own LDS-destination loads are outstanding
+    // ran 8% slower); the first half computes (only groups of more than 128
+    // rows compute on the second half too).  The stager takes a copy of the
+    // lane index that the compiler cannot identify with lane, so its per-lane
+    // offsets are computed here and not hoisted above the branch into a live
+    // range shared with the ping-pong's stager.  (Its wave count is spelled
+    // through SP so that kernels without the spread never instantiate it.)
+    constexpr int kStageWaves = SP ? NW / 2 : NW;
     int lane_x = lane;
     asm volatile("" : "+v"(lane_x));
-    auto dst = make_direct(lane_x);
+    PagedDirectStager<D, kStageWaves, C::kKPage> dst;
+    {
+      const int64_t head_off = (int64_t)g * p.head_stride * G::kEs;
+      dst.init(wv % kStageWaves, lane_x, static_cast<const unsigned char*>(p.k) + head_off,
+               static_cast<const unsigned char*>(p.v) + head_off, table, p.num_pages,
+               p.page_stride * G::kEs, (uint32_t)(p.token_stride * G::kEs), lk, p.max_pages);
+    }
     using St = decltype(dst);
-    static_assert(St::kWavesPerPage == 2, "two waves per page region");
-    constexpr int kL0 = St::loads_per_block(0), kL1 = St::loads_per_block(1);
+    static_assert(St::kWavesPerPage == 1, "one staging wave per page region");
+    const bool stager = wv >= NW - kStageWaves;
+    constexpr int kLoads = St::loads_per_block(0);  // per staging wave and block
     auto kst = [&](int sidx) { return sidx == 2 ? sQ + kSt2 : sK + sidx * C::kKStage; };
     auto vst = [&](int sidx) { return sidx == 2 ? sQ + kSt2 + C::kKStage : sV + sidx * C::kVStage; };
     int ebase = blk_begin;
@@ -1107,8 +1123,10 @@ void prefill_kernel(const PrefillParams p) {
     };
     for (int b = 0; b < ns - 1 && b < n; ++b) {
       dst.use_entry(entry(blk_begin + b));
-      dst.issue_k(blk_begin + b, kst(b), wv);
-      dst.issue_v(blk_begin + b, vst(b), wv);
+      if (stager) {
+        dst.issue_k(blk_begin + b, kst(b), wv);
+        dst.issue_v(blk_begin + b, vst(b), wv);
+      }
     }
     for (int x = tid; x < C::kTileRows * G::kChunks16; x += C::kThreads) {
       const int r = x / G::kChunks16, col = x % G::kChunks16;
@@ -1124,7 +1142,7 @@ void prefill_kernel(const PrefillParams p) {
       const int blk = blk_begin + j;
       const int ahead_st = cur == 0 ? ns - 1 : cur - 1;
       const bool ahead = j + ns - 1 < n;
-      if (ahead) {
+      if (ahead && stager) {
         dst.use_entry(entry(blk + ns - 1));
         dst.template issue_k<true>(blk + ns - 1, kst(ahead_st), wv);
         dst.template issue_v<true>(blk + ns - 1, vst(ahead_st), wv);
@@ -1138,14 +1156,10 @@ void prefill_kernel(const PrefillParams p) {
         pv_accumulate<D, NT>(acc, dt0, alpha, pb, vst(cur), lane);
       }
       if ((blk + 1) % kBlocksPerChunk == 0 || blk + 1 == blk_end) end_chunk(blk / kBlocksPerChunk);
-      // Block j+1 has landed; with three stages this wave's loads of block
-      // j+2 (issued last) may stay outstanding.
-      if (ahead && deep) {
-        if (dst.sub == 0) {
-          wait_vm_n<kL0>();
-        } else {
-          wait_vm_n<kL1>();
-        }
+      // Block j+1 has landed; with three stages a staging wave's loads of
+      // block j+2 (issued last) may stay outstanding.
+      if (ahead && deep && stager) {
+        wait_vm_n<kLoads>();
       } else {
         wait_vm();
       }
@@ -1173,7 +1187,7 @@ void prefill_kernel(const PrefillParams p) {
     // earlier in the same stage and before the first read of its own block.
     const int n = blk_end - blk_begin;
     const int lag = wv >= NW / 2 ? 1 : 0;
-    auto dst = make_direct(lane);
+    auto dst = make_direct();
     // event e: K block e+1 -> K stage (e+1)&1, V block e -> V stage e&1 (relative
     // blocks).  A wave's events run in order, so after issuing event e it looks
     // up (paged caches) the blocks of event e+1.
@@ -1247,7 +1261,7 @@ void prefill_kernel(const PrefillParams p) {
                  kv_row_bytes, tid);
       }
     };
-    auto dst = make_direct(lane);
+    auto dst = make_direct();
     if constexpr (C::kDirect) {
       dst.prefetch(blk_begin, blk_begin);
       dst.latch();
