@@ -144,7 +144,7 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
 }
 
 // ---- MFMA -----------------------------------------------------------------
-// v_mfma_f32_32x32x16_{bf16,fp8_fp8}: A is 32x16, lane l supplies
+// v_mfma_f32_32x32x16_bf16: A is 32x16, lane l supplies
 // A[l % 32][8*(l/32) .. +7]; B is 16x32, lane l supplies B[8*(l/32) .. +7][l % 32];
 // D is 32x32, lane l holds D[8*(i/4) + 4*(l/32) + i%4][l % 32] in element i.
 __device__ __forceinline__ f32x16 mfma_bf16(u32x4 a, u32x4 b, f32x16 c) {
