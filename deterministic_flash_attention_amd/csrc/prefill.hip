@@ -7,12 +7,22 @@
 // shows what a K stage landing in a live Q tile does).  Keys are folded in
 // 512-key chunks exactly as contract.hpp prescribes.
 //
-// bf16 K and V go from HBM straight into the padded LDS stages (buffer loads
-// with an LDS destination, no staging registers); fp8 goes through registers
-// because V is widened to bf16 on the way.  With eight bf16 waves the two
-// halves of the workgroup ping-pong (one in its MFMA phase while the other
-// runs its softmax, two barriers per block); otherwise every wave runs the
-// block in lockstep with block j+1 in flight and one barrier per block.
+// bf16 K and V (and e4m3 K from packed rows) go from HBM straight into the
+// padded LDS stages (buffer loads with an LDS destination, no staging
+// registers); e4m3 V goes through registers because it is widened to bf16 on
+// the way.  Block schedules:
+//   ping-pong   eight bf16 waves, D <= 128: the two halves of the workgroup
+//               alternate (one in its MFMA phase while the other runs its
+//               softmax, two barriers per block);
+//   pair        e4m3 D = 192 from packed rows: of the two waves sharing a SIMD
+//               and 32 query rows, one computes the scores and softmax once
+//               for both and hands P over through LDS;
+//   lockstep    the other layouts: every wave runs the block with block j+1
+//               in flight and one barrier per block.
+// Over a paged cache a single-token sequence packs the query heads of its kv
+// group into one tile set; with a workspace its chunks spread over otherwise
+// idle workgroups, whose bf16 tiles run a block loop of their own (three K/V
+// stages, the staging on the second half of the waves).
 //
 // Schedules (RL-Kernel page, section 2):
 //   monolithic  the workgroup folds every chunk of its tile in registers and
