@@ -703,9 +703,13 @@ void prefill_kernel(const PrefillParams p) {
     // score wave to tiles [0, kPairTilesS), the PV wave, which reads P_{j-1} from
     // its slot, to the other kPairTilesV.  The PV waves do all the staging
     // through registers, in two register sets used on alternate steps: step j
-    // loads K_{j+3} and V_{j+1} into set (j+1) % 2, then writes K_{j+2} into K
-    // stage (j+2) % 3 and V_j, widened to bf16, into V stage j % 2 from set
-    // j % 2 (loaded in step j - 1, so a load has a whole step to arrive).
+    // loads K_{j+3} and V_{j+1} into set (j+1) % 2, issues its P V of block
+    // j - 1, then writes K_{j+2} into K stage (j+2) % 3 and V_j, widened to
+    // bf16, into V stage j % 2 from set j % 2 (loaded in step j - 1, so a load
+    // has a whole step to arrive).  The widening comes after the P V MFMAs so
+    // that it runs under them, beside the score wave's softmax, and the
+    // SIMD's matrix work is not all at the start and end of the step (writing
+    // the stages first was 2.5% slower).
     // Slot use in step j: K stage (j+1) % 3 is read (written in step j - 1) and
     // K stage (j+2) % 3 written (last read in step j - 2); V stage (j-1) % 2 read
     // (written in step j - 1), V stage j % 2 written (last read in step j - 1);
@@ -897,8 +901,6 @@ void prefill_kernel(const PrefillParams p) {
             // leave this step's loads outstanding.
             load(kr, blk + 3, kreg[X ^ 1]);
             load(vr, blk + 1, vreg[X ^ 1]);
-            k_store(kstage(j + 2), kreg[X]);
-            v_store(sVp + X * C::kVStage, vreg[X]);
             if (j > 0 && wave_live(blk - 1)) {
               const unsigned char* const ps = pslot(j - 1);
               u32x4 pb[4];
@@ -910,6 +912,8 @@ void prefill_kernel(const PrefillParams p) {
               rescale_acc<NTX>(acc, bits_f32(st[0]));
               pv_mfma<D, NTX>(acc, NTS, pb, sVp + (X ^ 1) * C::kVStage, lane);
             }
+            k_store(kstage(j + 2), kreg[X]);
+            v_store(sVp + X * C::kVStage, vreg[X]);
             if constexpr (!SPLIT) {
               if (chunk_end) {
                 fold(m, l);
