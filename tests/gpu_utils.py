@@ -81,10 +81,11 @@ def run_extend(inp: synth.ExtendInputs, schedule: int, return_lse: bool = False,
     return res
 
 
-def oracle_extend(inp: synth.ExtendInputs, rows=None):
+def oracle_extend(inp: synth.ExtendInputs, rows=None, window=(-1, -1)):
     """fp64 oracle of a paged extend batch: each sequence's keys gathered from
     its pages by the oracle (over the sequence's own pages, widened to fp64),
-    then the packed-varlen definition with bottom-right alignment."""
+    then the packed-varlen definition with bottom-right alignment (and the
+    sliding window, if given)."""
     ps = inp.page_size
 
     ks, vs = [], []
@@ -105,7 +106,7 @@ def oracle_extend(inp: synth.ExtendInputs, rows=None):
         q = synth.to_f64(inp.q)
     return oracle.attention(q, np.concatenate(ks), np.concatenate(vs), inp.cu_seqlens_q.numpy(),
                             inp.cu_full.numpy(), inp.hq, inp.hkv, inp.scale, inp.causal,
-                            rows=rows)
+                            rows=rows, window=window)
 
 
 def compare(gpu_o: torch.Tensor, ref: np.ndarray, fp8: bool, rows=None, label: str = ""):

@@ -1,0 +1,151 @@
+"""Seeded sweep of small random configurations through the three attention
+entry points, each against the fp64 oracle element by element and, where two
+schedules exist, split against monolithic bit for bit: head dims 64 / 128 /
+192, bf16 and e4m3, kv groups of 1 to 16 query heads, ragged lengths around
+the 64-key block and 512-key chunk edges, causal or not, sliding windows, and
+prefix-cached extends over a paged cache with and without the chunk-spread
+workspace.  Fixed cases pin known edges; these draw combinations no fixed case
+lists (RL-Kernel page, section 2: one arithmetic path for every caller)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_utils import (assert_bitwise, compare, dev, extend_workspace, note,
+                       oracle_extend, oracle_inputs_prefill, run_decode, run_extend)
+
+pytestmark = pytest.mark.gpu
+
+MONO, SPLIT = 0, 1
+EDGE_LENS = [1, 2, 63, 64, 65, 127, 300, 511, 512, 513, 700]
+
+
+def _draw(rng, choices):
+    return choices[int(rng.integers(len(choices)))]
+
+
+def _common(rng):
+    d = _draw(rng, [64, 128, 192])
+    dtype = _draw(rng, ["bf16", "fp8"])
+    hkv = _draw(rng, [1, 2])
+    group = _draw(rng, [1, 2, 4, 8, 16])
+    return d, dtype, group * hkv, hkv
+
+
+def _window(rng):
+    r = rng.random()
+    if r < 0.6:
+        return (-1, -1)
+    if r < 0.8:
+        return (int(rng.integers(0, 600)), -1)
+    if r < 0.9:
+        return (-1, int(rng.integers(0, 200)))
+    return (int(rng.integers(0, 400)), int(rng.integers(0, 100)))
+
+
+def _check_lse(lse, ref_lse):
+    lg = lse.cpu().double().numpy()
+    assert np.array_equal(np.isneginf(lg), np.isneginf(ref_lse)), "lse -inf pattern differs"
+    fin = np.isfinite(ref_lse)
+    if fin.any():
+        assert np.abs(lg[fin] - ref_lse[fin]).max() < 2e-3
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_random_prefill(case):
+    import deterministic_flash_attention_amd as dfa
+    rng = np.random.default_rng(7000 + case)
+    d, dtype, hq, hkv = _common(rng)
+    b = int(rng.integers(1, 4))
+    sq = [_draw(rng, EDGE_LENS) for _ in range(b)]
+    extend = rng.random() < 0.4
+    sk = [q + _draw(rng, [0, 1, 64, 450, 513]) for q in sq] if extend else None
+    causal = bool(rng.random() < 0.6)
+    win = _window(rng)
+    inp = synth.prefill_inputs(7000 + case, sq, hq, hkv, d, causal, seqlens_k=sk, dtype=dtype)
+    note(f"random prefill {case}: {dtype} d={d} hq={hq} hkv={hkv} q={sq} k={sk} "
+         f"causal={causal} window={win}")
+    outs = []
+    for sched in (MONO, SPLIT):
+        o, lse = dfa.prefill(dev(inp.q), dev(inp.k), dev(inp.v), dev(inp.cu_seqlens_q),
+                             dev(inp.cu_seqlens_k), max(inp.seqlens_q), max(inp.seqlens_k),
+                             causal, softmax_scale=inp.scale, schedule=sched,
+                             descales=(inp.q_scale, inp.k_scale, inp.v_scale), window=win,
+                             return_lse=True)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    q, k, v = oracle_inputs_prefill(inp)
+    ref, ref_lse = oracle.attention(q, k, v, inp.cu_seqlens_q.numpy(), inp.cu_seqlens_k.numpy(),
+                                    hq, hkv, inp.scale, causal, window=win)
+    compare(outs[0][0], ref, dtype == "fp8", label=f"O case {case}")
+    _check_lse(outs[0][1], ref_lse)
+    assert_bitwise(outs[1][0], outs[0][0], "O split vs monolithic")
+    assert_bitwise(outs[1][1], outs[0][1], "lse split vs monolithic")
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_random_paged_extend(case):
+    rng = np.random.default_rng(8000 + case)
+    d, dtype, hq, hkv = _common(rng)
+    b = int(rng.integers(1, 5))
+    ql, ctx = [], []
+    for _ in range(b):
+        kind = rng.random()
+        if kind < 0.4:    # decode row
+            ql.append(1)
+            ctx.append(int(rng.integers(1, 3000)))
+        elif kind < 0.7:  # extend of a cached prefix
+            q = _draw(rng, EDGE_LENS)
+            ql.append(q)
+            ctx.append(q + int(rng.integers(0, 1500)))
+        else:             # prefill
+            q = _draw(rng, EDGE_LENS)
+            ql.append(q)
+            ctx.append(q)
+    causal = bool(rng.random() < 0.8)
+    win = _window(rng)
+    inp = synth.extend_inputs(8000 + case, ctx, ql, hq, hkv, d, causal=causal, dtype=dtype)
+    note(f"random paged extend {case}: {dtype} d={d} hq={hq} hkv={hkv} q={ql} ctx={ctx} "
+         f"causal={causal} window={win}")
+    o, lse = run_extend(inp, MONO, return_lse=True, window=win)
+    ref, ref_lse = oracle_extend(inp, window=win)
+    compare(o, ref, dtype == "fp8", label=f"O case {case}")
+    _check_lse(lse, ref_lse)
+    o_s, lse_s = run_extend(inp, SPLIT, return_lse=True, window=win)
+    assert_bitwise(o_s, o, "O split vs monolithic")
+    assert_bitwise(lse_s, lse, "lse split vs monolithic")
+    o_w, lse_w = run_extend(inp, MONO, return_lse=True, window=win,
+                            workspace=extend_workspace(inp))
+    assert_bitwise(o_w, o, "O with the spread workspace vs without")
+    assert_bitwise(lse_w, lse, "lse with the spread workspace vs without")
+
+
+@pytest.mark.parametrize("case", range(20))
+def test_random_decode(case):
+    rng = np.random.default_rng(9000 + case)
+    d = _draw(rng, [64, 128, 192])
+    dtype = _draw(rng, ["bf16", "fp8"])
+    hkv = _draw(rng, [1, 2, 4])
+    hq = hkv * _draw(rng, [1, 2, 4, 8, 32])
+    b = int(rng.integers(1, 9))
+    ctx = [int(rng.integers(0, 2500)) for _ in range(b)]
+    ctx[0] = max(ctx[0], 1)  # at least one key in the launch
+    inp = synth.decode_inputs(9000 + case, b, hq, hkv, d, context_lens=ctx, spare_pages=16,
+                              dtype=dtype)
+    note(f"random decode {case}: {dtype} d={d} hq={hq} hkv={hkv} ctx={ctx}")
+    o, lse = run_decode(inp, SPLIT, return_lse=True)
+    if dtype == "fp8":
+        q = oracle.dequantize_e4m3(inp.q.numpy(), inp.q_scale)
+        kc = oracle.dequantize_e4m3(inp.k_cache.numpy(), inp.k_scale)
+        vc = oracle.dequantize_e4m3(inp.v_cache.numpy(), inp.v_scale)
+    else:
+        q, kc, vc = synth.to_f64(inp.q), inp.k_cache.float().numpy(), inp.v_cache.float().numpy()
+    ref, ref_lse = oracle.paged_decode(q, kc, vc, inp.page_table.numpy(),
+                                       inp.context_lens.numpy(), hq, hkv, inp.scale,
+                                       inp.page_size)
+    compare(o, ref, dtype == "fp8", label=f"decode O case {case}")
+    _check_lse(lse, ref_lse)
+    o_m, lse_m = run_decode(inp, MONO, return_lse=True)
+    assert_bitwise(o_m, o, "decode O monolithic vs split")
+    assert_bitwise(lse_m, lse, "decode lse monolithic vs split")
