@@ -16,15 +16,21 @@
 //     instruction shape and the K order are part of the contract, as the same
 //     page says of its GEMM sibling (section 1);
 //   * scores are masked by select (to -inf), never by adding; the block max is
-//     m_blk = c * max(raw scores) with c = scale * q_descale * k_descale * log2(e),
-//     m' = max(m, m_blk), alpha = exp2(m - m'), p = exp2(fma(s, c, -m')) with
-//     v_exp_f32 and one explicit fused multiply-add, a fixed row-sum tree,
-//     l = l*alpha + sum(p); a row whose block is fully masked keeps
-//     m, l and acc bit for bit (alpha = 1, p = 0, and its empty state uses the
-//     safe max 0 so no -inf - -inf appears);
+//     m_blk = c * max(raw scores) with c = scale * q_descale * k_descale * log2(e);
+//     the row's reference m moves to m_blk only when m_blk > m + 8 (always from
+//     the empty state's -inf), so m' is m_blk or m and every p of a chunk is at
+//     most about 2^8; alpha = exp2(m - m'), or 1 when m = -inf (the state is empty, l
+//     and acc are zeros, and a factor of 0 or 1 leaves them the same bits);
+//     p = exp2(fma(s, c, -m')) with v_exp_f32 and one explicit fused
+//     multiply-add, a fixed row-sum tree, l = l*alpha + sum(p); a row whose
+//     block is fully masked keeps m, l and acc bit for bit (alpha = 1, p = 0,
+//     and its empty state uses the safe max 0 so no -inf - -inf appears);
 //   * P is rounded to bf16 (nearest even) and acc = (acc*alpha) + P V on
 //     v_mfma_f32_32x32x16_bf16, four 16-key K-steps in ascending key order; fp8
-//     V is widened exactly to bf16 first;
+//     V is widened exactly to bf16 first.  A wave whose lanes all hold alpha = 1
+//     skips the products acc*alpha (x * 1 is x): with the threshold of 8 a
+//     chunk's reference rarely moves after its first visible block, so most
+//     blocks skip them;
 //   * chunk partials (m_c, l_c, acc_c) are folded left to right in ascending
 //     chunk order with the exact max/sum rescale (a skipped empty partial, a
 //     copy into an empty total, or M' = max(M, m_c), a = exp2(M - M'),
@@ -61,6 +67,8 @@ constexpr int kBlockKeys = 64;
 constexpr int kChunkKeys = 512;
 constexpr int kBlocksPerChunk = kChunkKeys / kBlockKeys;
 constexpr uint32_t kParked = 0x80000000u;  // store offset past every num_records
+// A row's softmax reference moves up only past this margin (log2 units).
+constexpr float kRaiseLog2 = 8.0f;
 
 template <int D, bool FP8>
 struct Geom {
@@ -257,10 +265,13 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
   // Phase 2: the other half-wave (lane ^ 32) holds the remaining 32 keys.
   mr = half_wave_max(mr);
   const float mb = mr * c;
-  const float mn = fmaxf(m, mb);
+  // The reference moves only when the block's max passes it by more than
+  // kRaiseLog2; otherwise alpha = exp2(0) = 1 and p stays at most about
+  // 2^kRaiseLog2.
+  const float mn = (mb > m + kRaiseLog2) ? mb : m;
   const bool empty = (mn == -INFINITY);
   const float nms = empty ? 0.0f : -mn;
-  alpha = empty ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+  alpha = (m == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
   // Phases 3-4: p = exp2(c * s - m'), product and difference in one explicit
   // fused multiply-add (one rounding); masked scores are -inf and give p = 0.
 #pragma unroll
@@ -291,8 +302,9 @@ __device__ __forceinline__ void softmax_block(const f32x16 (&s)[2], int h, float
 }
 
 // acc_j = acc_j * alpha, the first half of the accumulator update.
-template <int NT>
+template <int NT, bool SKIP = true>
 __device__ __forceinline__ void rescale_acc(f32x16 (&acc)[NT], float alpha) {
+  if (SKIP && __builtin_amdgcn_ballot_w64(alpha != 1.0f) == 0) return;  // x * 1 is x
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
@@ -323,11 +335,11 @@ __device__ __forceinline__ void pv_mfma(f32x16 (&acc)[NT], int dt0, const u32x4 
 }
 
 // acc_j = acc_j * alpha + P V: both halves back to back.
-template <int D, int NT>
+template <int D, int NT, bool SKIP = true>
 __device__ __forceinline__ void pv_accumulate(f32x16 (&acc)[NT], int dt0, float alpha,
                                               const u32x4 (&pb)[4], const unsigned char* vs,
                                               int lane) {
-  rescale_acc<NT>(acc, alpha);
+  rescale_acc<NT, SKIP>(acc, alpha);
   pv_mfma<D, NT>(acc, dt0, pb, vs, lane);
 }
 

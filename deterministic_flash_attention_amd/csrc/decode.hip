@@ -266,7 +266,7 @@ __global__ __launch_bounds__(D / 32 * 64) void decode_kernel(const DecodeParams 
         m = bits_f32(st[1]);
         l = bits_f32(st[2]);
         if (more) stg.store_k(sK, tid);
-        pv_accumulate<D, 1>(acc, wave, bits_f32(st[0]), pb, sV, lane);
+        pv_accumulate<D, 1, false>(acc, wave, bits_f32(st[0]), pb, sV, lane);
         __syncthreads();  // every wave is done with the P slot and the V stage
         if (more) {
           stg.store_v(sV, tid);

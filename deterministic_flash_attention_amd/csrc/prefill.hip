@@ -1223,9 +1223,11 @@ void prefill_kernel(const PrefillParams p) {
     __syncthreads();
     if (lag) __syncthreads();
     const unsigned char* const sQw = sQ + (32 * qg) * G::kQRow;
-    // bf16: the wave's Q^T operands move from the LDS tile to registers once.
+    // bf16 from packed rows: the wave's Q^T operands move from the LDS tile to
+    // registers once.  Over a paged cache they are read from the tile every
+    // block, which leaves the registers that the paged staging holds.
     QOperands<D, FP8> qop;
-    if constexpr (!FP8) qop.load(sQw + (lane & 31) * G::kQRow, lane);
+    if constexpr (!FP8 && !PAGED) qop.load(sQw + (lane & 31) * G::kQRow, lane);
     u32x4 pb[4];
     for (int j = 0; j < n; ++j) {
       const int blk = blk_begin + j;
@@ -1236,7 +1238,7 @@ void prefill_kernel(const PrefillParams p) {
       }
       f32x16 s[2];
       if (live) {
-        if constexpr (FP8) {
+        if constexpr (FP8 || PAGED) {
           qk_scores_qlds<D, FP8, C::kKPage>(s, sQw, sK + (j & 1) * C::kKStage, lane);
         } else {
           qk_scores_qreg<D, FP8, C::kKPage>(s, qop, sK + (j & 1) * C::kKStage, lane);
