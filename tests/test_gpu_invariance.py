@@ -304,3 +304,61 @@ def test_zero_sign_under_alpha_underflow():
     from gpu_utils import run_extend
     for sched in (MONO, SPLIT):
         assert_bitwise(run_extend(pext, sched).cpu(), o_pre[1:], f"paged extend (schedule {sched})")
+
+
+def _threshold_inputs():
+    """One head, D = 64, 1024 keys (two chunks), no mask.  Query row 300 holds
+    8 in dimension 0 and zeros elsewhere; in dimension 0 every key is zero
+    except one key per block, so in log2 units (scale 1/8, c = log2(e)/8) row
+    300's block maxima are 1.4427 * 8 * y for the chosen y.  Within chunk 0 the
+    reference starts at 0 and the maxima pass it by 7.93 (no move: P reaches
+    2^7.93), 8.02 (a move), 7.93 and 8.02 again, then by 0 and 6.94 (no moves)
+    before falling; chunk 1 starts from the empty state and repeats a no-move /
+    move pair.  Every y is exact in bf16 and every decision has a margin of at
+    least 0.025 over the fp32 roundings."""
+    n, d, r = 1024, 64, 300
+    inp = synth.prefill_inputs(83, [n], 1, 1, d, False)
+    q, k = inp.q.clone(), inp.k.clone()
+    q[r, 0] = 0.0
+    q[r, 0, 0] = 8.0
+    k[:, 0, 0] = 0.0
+    ys = [0.0, 5.5, 5.5625, 11.0625, 11.125, 11.125, 15.9375, 2.0,
+          2.0, 7.5, 7.5625, 0.0, 0.0, 0.0, 0.0, 0.0]
+    for b, y in enumerate(ys):
+        k[64 * b + 17, 0, 0] = y
+    return synth.PrefillInputs(q, k, inp.v, synth.cu_seqlens([n]), synth.cu_seqlens([n]), [n], [n],
+                               1, 1, d, inp.scale, False), r
+
+
+def test_reference_threshold_edges():
+    """The softmax reference moves only when a block's max passes it by more
+    than 8 (log2 units); just below, P reaches 2^7.93 and the accumulator is
+    not rescaled.  Against the oracle (the bound of the bf16 arithmetic,
+    2^-8 (max|v| + |O|), as for the peaky rows), split = monolithic, and the
+    decode of row 300 over a paged copy of the keys equals its prefill row."""
+    import oracle
+    from gpu_utils import oracle_inputs_prefill
+    inp, r = _threshold_inputs()
+    n, d = inp.q.shape[0], inp.q.shape[2]
+    o_mono, lse = run_prefill(inp, MONO, return_lse=True)
+    o_split = run_prefill(inp, SPLIT)
+    assert_bitwise(o_split.cpu(), o_mono.cpu(), "split vs monolithic")
+    q, k, v = oracle_inputs_prefill(inp)
+    ref, ref_lse = oracle.attention(q, k, v, inp.cu_seqlens_q.numpy(), inp.cu_seqlens_k.numpy(),
+                                    1, 1, inp.scale, False)
+    g = o_mono.float().cpu().double().numpy()
+    bound = 1.05 * 2.0**-8 * (float(np.abs(v).max()) + np.abs(ref)) + 1e-6
+    err = np.abs(g - ref)
+    note(f"threshold edges: row {r} max_abs={err[r].max():.3e}, all rows max err/bound="
+         f"{float((err / bound).max()):.3f}")
+    assert np.isfinite(g).all() and (err <= bound).all(), "beyond the bf16 arithmetic's bound"
+    lse_err = np.abs(lse.cpu().double().numpy() - ref_lse)
+    assert float(lse_err.max()) <= 2e-3, f"lse error {lse_err.max()}"
+    ps = 16
+    kc = inp.k.reshape(n // ps, ps, 1, d).contiguous()
+    vc = inp.v.reshape(n // ps, ps, 1, d).contiguous()
+    table = torch.arange(n // ps, dtype=torch.int32).reshape(1, n // ps)
+    dec = synth.DecodeInputs(inp.q[r:r + 1].contiguous(), kc, vc, table,
+                             torch.tensor([n], dtype=torch.int32), 1, 1, d, ps, inp.scale)
+    for sched in (SPLIT, MONO):
+        assert_bitwise(run_decode(dec, sched).cpu()[0], o_mono.cpu()[r], f"decode (schedule {sched})")
