@@ -511,16 +511,25 @@ void prefill_kernel(const PrefillParams p) {
     id /= p.hq;
   }
   int b = id % p.batch;
+  // Sequence bounds of this workgroup's sequence, read below unless the sort
+  // has them in LDS already.
+  bool bounds_lds = false;
+  int lds_q0 = 0, lds_q1 = 0, lds_ctx = 0;
   if constexpr (PAGED && !SPLIT) {
     // A mixed batch can hold a decode or short extend whose single tile scans a
     // long context; handed out last, that tile alone would run past everything
     // else.  Sequences are therefore dealt in descending context length (ties by
     // index): the rank-th longest sequence takes this workgroup's batch slot.
-    // Which workgroup computes a tile changes no bit of its result.
+    // Which workgroup computes a tile changes no bit of its result.  The query
+    // offsets are read beside the context lengths, so the sequence's bounds
+    // need no second memory round trip after the sort.
     __shared__ int sCtx[C::kThreads];
+    __shared__ int sCuq[C::kThreads];
     __shared__ int sSeq;
     if (p.batch <= C::kThreads) {
+      bounds_lds = p.batch < C::kThreads;  // cu_q has batch + 1 entries
       if (tid < p.batch) sCtx[tid] = p.ctx_lens[tid];
+      if (bounds_lds && tid <= p.batch) sCuq[tid] = p.cu_q[tid];
       __syncthreads();
       if (tid < p.batch) {
         const int key = sCtx[tid];
@@ -532,7 +541,12 @@ void prefill_kernel(const PrefillParams p) {
         if (rank == b) sSeq = tid;
       }
       __syncthreads();
-      b = sSeq;
+      b = uniform(sSeq);
+      if (bounds_lds) {
+        lds_q0 = uniform(sCuq[b]);
+        lds_q1 = uniform(sCuq[b + 1]);
+        lds_ctx = uniform(sCtx[b]);
+      }
     }
   }
   id /= p.batch;
@@ -543,13 +557,13 @@ void prefill_kernel(const PrefillParams p) {
   }
   const int tile_rev = id;
 
-  const int q_start = uniform(p.cu_q[b]);
-  const int lq = uniform(p.cu_q[b + 1]) - q_start;
+  const int q_start = bounds_lds ? lds_q0 : uniform(p.cu_q[b]);
+  const int lq = (bounds_lds ? lds_q1 : uniform(p.cu_q[b + 1])) - q_start;
   // Keys: packed rows [cu_k[b], cu_k[b+1]), or the first ctx_lens[b] tokens of
   // the sequence's pages (clamped to its page-table row).
   int k_start = 0, lk;
   if constexpr (PAGED) {
-    lk = max(0, min(uniform(p.ctx_lens[b]), p.max_pages * 16));
+    lk = max(0, min(bounds_lds ? lds_ctx : uniform(p.ctx_lens[b]), p.max_pages * 16));
   } else {
     k_start = uniform(p.cu_k[b]);
     lk = uniform(p.cu_k[b + 1]) - k_start;
