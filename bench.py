@@ -152,7 +152,7 @@ def stats(rep_ms):
             "ms_rep_means": [round(m, 5) for m in means]}
 
 
-def prefill_line(name, cfg, causal, dtype, peak, peak_note, window=(-1, -1)):
+def prefill_line(name, cfg, causal, dtype, peak, peak_note, window=(-1, -1), traffic=None):
     import oracle
     inp, t = prefill_workload(cfg, causal, dtype)
     fn, _ = run_prefill_fn(inp, t, 0, window)
@@ -168,7 +168,8 @@ def prefill_line(name, cfg, causal, dtype, peak, peak_note, window=(-1, -1)):
             "flop": flops, **s, "value": tf, "unit": "TFLOP/s",
             "tflops_at_min": flops / (s["ms_min"] * 1e-3) / 1e12,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
-                         "frac": tf / peak, "traffic": None, "peak_note": peak_note},
+                         "frac": tf / peak, "traffic": counted_traffic(traffic) if traffic else None,
+                         "peak_note": peak_note},
         }
     return Line({"run": fn}, finish)
 
@@ -299,7 +300,8 @@ def extend_line():
             "single_tile_ms_median": st["single"]["ms_median"],
             "single_tile_tflops": flops / (st["single"]["ms_median"] * 1e-3) / 1e12,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS, "traffic": None,
+                         "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                         "traffic": counted_traffic("mixed_paged_extend"),
                          "kernel": "prefill_kernel<128, bf16, paged, monolithic, chunk spread>"},
         }
     return Line({"run": fn, "single": fn_single}, finish)
@@ -358,16 +360,17 @@ def secondary_lines():
     mixed = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
     lines = [
         prefill_line("causal_gqa_varlen", synth.CAUSAL_VARLEN, True, "bf16", PEAK_BF16_TFLOPS,
-                     "bf16 dense MFMA"),
+                     "bf16 dense MFMA", traffic="prefill_causal_varlen_bf16"),
         decode_line("bf16"),
         decode_line("fp8"),
         extend_line(),
         prefill_line("sliding_window_1024", synth.DENSE_PREFILL, True, "bf16", PEAK_BF16_TFLOPS,
-                     "bf16 dense MFMA", window=(1024, -1)),
+                     "bf16 dense MFMA", window=(1024, -1), traffic="sliding_window_1024"),
     ]
     for causal in (False, True):
         lines.append(prefill_line("fp8_wide_head", synth.FP8_WIDE, causal, "fp8", mixed,
-                                  "QK^T on fp8 MFMA, PV on bf16 MFMA: half the FLOPs at each peak"))
+                                  "QK^T on fp8 MFMA, PV on bf16 MFMA: half the FLOPs at each peak",
+                                  traffic="prefill_fp8_d192_" + ("causal" if causal else "dense")))
     for name, m, n, k in synth.GEMM_SHAPES:
         lines.append(gemm_line(name, m, n, k))
     return lines
@@ -428,8 +431,10 @@ def cpu_baseline(target_s: float = 12.0):
 def pmc_pass(kind: str):
     """Launches for counter runs (rocprofv3 --pmc), one dispatch per kernel in a
     fixed order printed to stdout.  "traffic": a copy of known size (256 MiB read,
-    256 MiB written) that calibrates FETCH_SIZE / WRITE_SIZE, then the dense
-    prefill, the bf16 and e4m3 decode split and merge, and the four GEMM shapes.
+    256 MiB written) that calibrates FETCH_SIZE / WRITE_SIZE, then the prefill
+    workloads (dense, causal GQA varlen, fp8 D=192 dense and causal, the sliding
+    window, the mixed paged batch), the bf16 and e4m3 decode split and merge, and
+    the four GEMM shapes.
     "prefill": the prefill workloads whose SQ counters the profiles quote
     (dense, causal GQA varlen, fp8 D=192 dense and causal, the mixed paged batch,
     the sliding window)."""
@@ -447,9 +452,18 @@ def pmc_pass(kind: str):
         src = torch.ones(128 << 20, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
         run("copy_256MiB", lambda: dst.copy_(src))
-        inp, t = prefill_workload(synth.DENSE_PREFILL, False, "bf16")
-        run("prefill_dense_bf16", run_prefill_fn(inp, t, dfa.MONOLITHIC)[0])
-        del inp, t
+        for label, cfg, causal, dt, win in (
+                ("prefill_dense_bf16", synth.DENSE_PREFILL, False, "bf16", (-1, -1)),
+                ("prefill_causal_varlen_bf16", synth.CAUSAL_VARLEN, True, "bf16", (-1, -1)),
+                ("prefill_fp8_d192_dense", synth.FP8_WIDE, False, "fp8", (-1, -1)),
+                ("prefill_fp8_d192_causal", synth.FP8_WIDE, True, "fp8", (-1, -1)),
+                ("sliding_window_1024", synth.DENSE_PREFILL, True, "bf16", (1024, -1))):
+            inp, t = prefill_workload(cfg, causal, dt)
+            run(label, run_prefill_fn(inp, t, dfa.MONOLITHIC, win)[0])
+            del inp, t
+        ln = extend_line()
+        run("mixed_paged_extend", ln.fns["run"])
+        del ln
         for dt in ("bf16", "fp8"):
             ln = decode_line(dt)
             run(f"decode_split_{dt}", ln.fns["split"])
@@ -481,7 +495,9 @@ def pmc_pass(kind: str):
 
 # Library dispatches of each counter pass, in launch order (see pmc_pass).
 PMC_LABELS = {
-    "traffic": ["prefill_dense_bf16", "decode_split_bf16", "merge_d128_bf16", "decode_split_fp8",
+    "traffic": ["prefill_dense_bf16", "prefill_causal_varlen_bf16", "prefill_fp8_d192_dense",
+                "prefill_fp8_d192_causal", "sliding_window_1024", "mixed_paged_extend",
+                "decode_split_bf16", "merge_d128_bf16", "decode_split_fp8",
                 "merge_d128_fp8", "gemm_gate_up", "gemm_down", "gemm_qkv_decode",
                 "gemm_qkv_decode_combine", "gemm_gate_up_decode", "gemm_gate_up_decode_combine"],
     "prefill": ["prefill_dense_bf16", "prefill_causal_varlen_bf16", "prefill_fp8_d192_dense",
